@@ -1,0 +1,34 @@
+"""CPU oracle for the fused exact-attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+anything from this package.  The product path (the HIP library and its Python
+binding) never imports, calls or links it, and the two share no code.
+
+Modules
+-------
+attention  plain two-pass fp64 attention (numpy), the reference every GPU
+           result is compared with, plus the online-softmax recurrence in the
+           pages' own step order (used only to pin the two-pass form).
+brute      the textbook softmax definition written as scalar loops over
+           mpmath numbers, with no max-subtraction, for tiny inputs.
+
+Pages cited (the text of three web pages on one subject):
+  [CANN-FA]  "FlashAttention operator of the CANN ops-transformer repository:
+             attention acceleration on the Ascend NPU", www.mooersco.com/news/1200175
+  [FA-Dict]  hwcomputing.csdn.net tutorial page 6a0dbd08662f9a54cb75eb74
+             (the "dictionary page by page" explanation of FlashAttention)
+  [FA-Infer] gitcode.csdn.net page 6a0c62d2662f9a54cb75b31f (why Transformer
+             inference is slow; FlashAttention on Ascend and CANN)
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+against closed forms, invariants, brute force and mutation tests; none is
+"parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    attention_ref,
+    attention_probs,
+    online_attention,
+    kv_head_of,
+)
