@@ -1,0 +1,146 @@
+"""Thin Python binding of libattn_fwd.so (argument marshalling only).
+
+Every step of the attention forward runs in the HIP kernels behind the C ABI
+declared in include/attn_fwd.h.  This module only checks tensor metadata,
+allocates outputs with torch (device memory), passes raw pointers and torch's
+current HIP stream, and turns status codes into exceptions.  There is no
+fallback: if the library is missing or the tensors are not on an AMD GPU, the
+call fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from .build import LIB_PATH
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_DEVICE = 3
+
+EXPORTS = ("attn_fwd", "attn_check_args", "attn_status_string", "attn_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn_fwd status {status}: {message}")
+        self.status = status
+
+
+class AttnUnsupportedError(AttnError, NotImplementedError):
+    """head_dim outside {64, 128, 256}; the caller may use an unfused path."""
+
+
+class AttnArgumentError(AttnError, ValueError):
+    """Invalid argument (see attn_check_args)."""
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libattn_fwd.so once and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -m exact_attention_121_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(p)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                             ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float]
+    lib.attn_check_args.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> str:
+    return load_library().attn_version().decode()
+
+
+def attn_check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, scale) -> int:
+    """Host-only validation (pointers as integers or None); returns a status."""
+    return load_library().attn_check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, float(scale))
+
+
+def _raise_for(status: int):
+    if status == ATTN_OK:
+        return
+    msg = attn_status_string(status)
+    if status == ATTN_ERR_UNSUPPORTED:
+        raise AttnUnsupportedError(status, msg)
+    if status == ATTN_ERR_INVALID_ARG:
+        raise AttnArgumentError(status, msg)
+    raise AttnError(status, msg)
+
+
+def attn_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, out=None,
+             lse=None, return_lse: bool = True, stream=None):
+    """Fused attention forward on torch fp16 tensors resident on one AMD GPU.
+
+    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous torch.float16 on the
+    same HIP device.  scale defaults to 1/sqrt(d).  Returns (o, lse) with o
+    [B, Hq, N, d] fp16 and lse [B, Hq, N] fp32 (None if return_lse is False
+    and no lse buffer is given).  The kernel is queued on ``stream`` (a
+    torch.cuda.Stream) or on torch's current stream of q's device.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be torch.float16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on an AMD GPU (torch 'cuda' device), got {t.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != torch.float16 or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous fp16 tensor shaped like q on q's device")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, Hq, N) or lse.dtype != torch.float32
+                              or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, N] on q's device")
+
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = lib.attn_fwd(
+            q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
+            out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
+            B, Hq, Hkv, N, d, float(scale), 1 if causal else 0, s.cuda_stream or None)
+    _raise_for(status)
+    return out, lse

@@ -1,0 +1,115 @@
+/*
+ * attn_fwd.h - C ABI of the fused exact-attention forward pass for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation ([CANN-FA] section "Where is the bottleneck of standard
+ * attention"; [FA-Infer] section 2) is, per batch b and query head h,
+ *
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,
+ *     LSE_i = ln sum_{j visible to i} exp(scale * q_i . k_j),
+ *
+ * computed as one fused kernel in the tiled, online-softmax form the pages
+ * describe ([CANN-FA] sections "Tiling on the Ascend NPU" and "Concrete
+ * flow"; [FA-Dict] sections "FlashAttention page by page", "Online softmax"
+ * and "Fused kernel"): the N x N score matrix never reaches device memory.
+ *
+ * Pages cited:
+ *   [CANN-FA]  www.mooersco.com/news/1200175 - "FlashAttention operator of
+ *              the CANN ops-transformer repository: attention acceleration
+ *              on the Ascend NPU"
+ *   [FA-Dict]  hwcomputing.csdn.net/6a0dbd08662f9a54cb75eb74.html - the
+ *              "dictionary, page by page" FlashAttention tutorial
+ *   [FA-Infer] gitcode.csdn.net/6a0c62d2662f9a54cb75b31f.html - why
+ *              Transformer inference is slow; FlashAttention on Ascend/CANN
+ *
+ * Conventions shared by every entry point
+ *   - Layout ([CANN-FA] section "Calling FlashAttention from PyTorch" and
+ *     [FA-Dict] section "Calling" show (batch, heads, seq, head_dim) fp16
+ *     tensors): q and o are [B][Hq][N][d], k and v are [B][Hkv][N][d], all
+ *     IEEE binary16, densely packed in that order (row-major, no strides).
+ *     lse is [B][Hq][N] IEEE binary32.
+ *   - GQA / MQA ([FA-Infer] section 6): Hq must be a multiple of Hkv; query
+ *     head h reads key/value head h / (Hq / Hkv) (contiguous groups).
+ *   - head_dim ([CANN-FA], the closing note on head_dim): d must be 64, 128
+ *     or 256.  The pages fall back to unfused attention for other values;
+ *     this library instead returns ATTN_ERR_UNSUPPORTED and launches nothing.
+ *   - causal != 0: key j is visible to query i iff j <= i ([CANN-FA] section
+ *     "Calling FlashAttention from PyTorch", is_causal).  Queries and keys
+ *     have the same length N.
+ *   - Memory: every pointer is device memory on the current HIP device,
+ *     owned by the caller, which keeps it alive until the work queued on
+ *     `stream` has completed.  The library allocates nothing and keeps no
+ *     state between calls; calls from several host threads are safe.
+ *   - Asynchrony: attn_fwd only queues work on `stream` (NULL = the default
+ *     stream) and returns; it never synchronises.  A device fault surfaces at
+ *     the caller's next synchronisation.
+ *   - Errors: on any status other than ATTN_OK nothing has been launched and
+ *     the outputs are untouched.
+ */
+#ifndef ATTN_FWD_H_
+#define ATTN_FWD_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP runtime's stream handle type (hipStream_t is `struct ihipStream_t*`),
+ * declared here so that this header does not need the HIP headers. */
+struct ihipStream_t;
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, bad grouping, non-finite
+                               scale, overlapping output, size over limits */
+  ATTN_ERR_UNSUPPORTED = 2, /* head_dim not in {64, 128, 256} */
+  ATTN_ERR_DEVICE = 3       /* the HIP runtime refused the launch */
+};
+
+/*
+ * attn_fwd - fused attention forward.
+ *
+ *   q      [B][Hq][N][d]  fp16, read only
+ *   k, v   [B][Hkv][N][d] fp16, read only
+ *   o      [B][Hq][N][d]  fp16, written: every element exactly once
+ *   lse    [B][Hq][N]     fp32, written (natural log), or NULL to skip it
+ *   B, N   >= 0; B == 0 or N == 0 is an empty problem: ATTN_OK, nothing is
+ *          launched and no pointer is touched (they may then be NULL)
+ *   Hq, Hkv >= 1 with Hq % Hkv == 0
+ *   d      64, 128 or 256
+ *   scale  finite multiplier on q.k (1/sqrt(d) in the pages' usage,
+ *          [FA-Dict] sections "Fused kernel" and "Calling"); any finite
+ *          value, including 0 and negative values, is accepted
+ *   causal 0 or non-zero
+ *   stream HIP stream to queue the kernel on (NULL = default stream)
+ *
+ * Limits: N * d < 2^31 and B * Hq * ceil(N / 128) < 2^31.  The output o (and
+ * lse) must not overlap q, k, v or each other.
+ * Returns an attn_status value.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+             float scale, int causal, struct ihipStream_t* stream);
+
+/*
+ * attn_check_args - the argument validation of attn_fwd, on the host only.
+ * Pointers are compared with NULL and with each other's address ranges but
+ * never dereferenced; no HIP call is made, so it runs without a GPU.
+ * Returns the status attn_fwd would return before launching.
+ */
+int attn_check_args(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t N, int64_t d, float scale);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* Static version string of the library, e.g. "attn_fwd 0.1.0 gfx950". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H_ */
