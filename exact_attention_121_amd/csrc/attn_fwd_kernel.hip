@@ -20,25 +20,31 @@
 //
 // gfx950 mapping
 //   * 256 threads = 4 waves of 64; wave w owns query rows q0+32w .. q0+32w+31.
+//     Two workgroups share a CU (<= 256 registers per lane, 64 KB of LDS
+//     each), so every SIMD interleaves the matrix-core work of one wave with
+//     the softmax arithmetic of the other.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_f16: A = 32 keys x 16 dims from LDS, B = 16 dims x
 //     32 queries from registers.  In the 32x32 fp32 result, lane L holds query
 //     L%32 and the 16 keys 8*(r/4) + 4*(L/32) + r%4 (r = 0..15), so each
-//     query's row max and row sum are in-lane reductions plus one exchange
-//     with lane L^32.
+//     query's row max is an in-lane reduction plus one v_permlane32_swap with
+//     lane L^32, and its row sum stays a per-lane partial until the end.
 //   * The probabilities stay in registers and are the B operand of
 //     O^T += V^T P^T (same instruction).  The reduction index of that product
-//     may be permuted freely, so the B operand's eight slots of lane L simply
-//     take the lane's own score registers; the A operand must then pair slot
-//     j of lane group L/32 with key 8*(j/4) + 4*(L/32) + j%4 (+16 per half).
-//     V is stored transposed in LDS with key positions bits 2 and 3 swapped,
-//     which turns exactly that key set into 8 consecutive halfs: one 16-byte
-//     LDS read per operand.
-//   * K/V tiles are double-buffered in LDS: the global loads of tile j+1 are
-//     issued before tile j is computed and written to the other buffer after
-//     it ([CANN-FA] section "Ascend C implementation", double buffering so
-//     that data movement hides behind the matrix unit).
-//   * exp is exp2 with scale*log2(e) folded into one fused multiply-add.
+//     may be permuted freely, so the eight B slots of lane L simply take the
+//     lane's own probability registers; the A operand must then pair slot j of
+//     lane group L/32 with key 8*(j/4) + 4*(L/32) + j%4 (+16 per half).  Two
+//     ds_read_b64_tr_b16 transpose-reads fetch exactly those keys (4 each)
+//     from V kept in its natural [key][dim] layout.
+//   * K and V tiles move from device memory straight into LDS with
+//     buffer_load_dwordx4 ... lds (no register staging; reads past the end of
+//     the sequence return zeros), double-buffered: tile j+1 is in flight while
+//     tile j is computed ([CANN-FA] section "Ascend C implementation": load
+//     block j+1 while block j is computed so that data movement hides behind
+//     the matrix unit).  16-byte chunks are XOR-swizzled by row so that the
+//     matrix-operand reads hit distinct LDS banks.
+//   * exp is exp2 with scale*log2(e) folded into one fused multiply-add; the
+//     O rescale is skipped when no row of the wave raised its maximum.
 //   * Causal: key tiles entirely above a wave's diagonal are skipped; only
 //     tiles crossing the diagonal or the end of the sequence are masked.
 //   * Workgroup ids are remapped so that each of the 8 XCDs (each with its
@@ -56,14 +62,18 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4v lds_short4;
 
 constexpr int kThreads = 256;  // 4 waves of 64 lanes
 constexpr int kWaveRows = 32;  // query rows per wave
 constexpr int kBM = 128;       // query rows per workgroup
 constexpr float kLn2 = 0.69314718055994531f;
+// Buffer resource word 3 for raw (unformatted, stride 0) buffer access on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <int D>
 struct Cfg {
@@ -71,16 +81,11 @@ struct Cfg {
   static constexpr int NT = BN / 32;               // 32-key sub-tiles of S^T
   static constexpr int DC = D / 16;                // 16-dim k-steps of Q.K
   static constexpr int DT = D / 32;                // 32-dim row tiles of O^T
-  static constexpr int KS = D + 8;                 // K row stride in LDS (halfs)
-  static constexpr int VS = BN + 8;                // V^T row stride in LDS (halfs)
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int K_CHUNKS = BN * D / 8;  // 16-byte chunks per K tile
-  static constexpr int K_PER_THREAD = K_CHUNKS / kThreads;
-  static constexpr int V_UNITS = BN * D / 32;  // (4 keys x 8 dims) units per V tile
-  static_assert(K_CHUNKS % kThreads == 0, "K tile must split evenly");
-  static_assert(V_UNITS <= kThreads, "one V unit per thread at most");
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;  // chunk XOR mask
+  static constexpr int TILE_BYTES = BN * D * 2;    // one K (or V) tile
+  static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
+  static_assert(BN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
 struct Params {
@@ -94,72 +99,54 @@ struct Params {
   uint32_t q_sign;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
 };
 
-// Key position inside a V^T tile row: bits 2 and 3 of the key index swapped.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+// Byte offset of 16-byte chunk `c` of row `r` inside a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  return (r * Cfg<D>::CPR + (c ^ (r & Cfg<D>::SWZ))) * 16;
 }
 
+// Queue the copy of rows kv0 .. kv0+BN-1 of one K or V head into a swizzled
+// LDS tile.  Rows at or past N read as zeros (buffer range check).
 template <int D>
-__device__ __forceinline__ void load_kv(const _Float16* __restrict__ kb,
-                                        const _Float16* __restrict__ vb, int kv0, int N,
-                                        int tid, u32x4 (&kr)[Cfg<D>::K_PER_THREAD],
-                                        u32x4 (&vr)[4]) {
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, char* tile, int kv0,
+                                          int tid) {
   using C = Cfg<D>;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
-  for (int i = 0; i < C::K_PER_THREAD; ++i) {
-    const int id = tid + i * kThreads;
-    const int row = id / CPR, ch = id % CPR;
-    const int key = kv0 + row;
-    kr[i] = key < N ? *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + ch * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-  }
-  if (tid < C::V_UNITS) {
-    const int k0 = (tid / CPR) * 4, d0 = (tid % CPR) * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kv0 + k0 + i;
-      vr[i] = key < N ? *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + d0)
-                      : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int p = i * kThreads + tid;  // destination chunk; lanes of a wave are consecutive
+    const int row = p / C::CPR;
+    const int chunk = (p % C::CPR) ^ (row & C::SWZ);
+    const int src = ((kv0 + row) * D + chunk * 8) * 2;
+    char* dst = tile + (i * kThreads + (tid & ~63)) * 16;  // wave-uniform base
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, src, 0, 0, 0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_kv(_Float16* __restrict__ ks, _Float16* __restrict__ vts,
-                                         int tid, const u32x4 (&kr)[Cfg<D>::K_PER_THREAD],
-                                         const u32x4 (&vr)[4]) {
-  using C = Cfg<D>;
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < C::K_PER_THREAD; ++i) {
-    const int id = tid + i * kThreads;
-    const int row = id / CPR, ch = id % CPR;
-    *reinterpret_cast<u32x4*>(ks + row * C::KS + ch * 8) = kr[i];
-  }
-  if (tid < C::V_UNITS) {
-    const int k0 = (tid / CPR) * 4, d0 = (tid % CPR) * 8;
-    const int pos = vt_pos(k0);
-    // Transpose 4 keys x 8 dims into 8 dims x 4 keys.
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t lo = __builtin_amdgcn_perm(vr[1][j >> 1], vr[0][j >> 1], sel);
-      const uint32_t hi = __builtin_amdgcn_perm(vr[3][j >> 1], vr[2][j >> 1], sel);
-      *reinterpret_cast<u32x2*>(vts + (d0 + j) * C::VS + pos) = u32x2{lo, hi};
-    }
-  }
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ short4v tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+}
+
+__device__ __forceinline__ float xlane_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+__device__ __forceinline__ float xlane_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
 // One K/V tile for one wave: S^T = K Q^T, online softmax update, O^T += V^T P^T.
-template <int D, bool MASK, bool CAUSAL>
-__device__ __forceinline__ void tile_step(const _Float16* __restrict__ ks,
-                                          const _Float16* __restrict__ vts,
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void tile_step(const char* __restrict__ ks, const char* __restrict__ vs,
                                           const half8 (&qf)[Cfg<D>::DC],
                                           f32x16 (&oacc)[Cfg<D>::DT], float& m_run,
                                           float& l_run, float c, int kv0, int N, int qrow,
-                                          int lr, int g) {
+                                          int lane, bool mask) {
   using C = Cfg<D>;
+  const int lr = lane & 31, g = lane >> 5;
   f32x16 s[C::NT];
 #pragma unroll
   for (int t = 0; t < C::NT; ++t) s[t] = f32x16{};
@@ -167,19 +154,22 @@ __device__ __forceinline__ void tile_step(const _Float16* __restrict__ ks,
   for (int dc = 0; dc < C::DC; ++dc) {
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
-      const half8 a = *reinterpret_cast<const half8*>(ks + (32 * t + lr) * C::KS + 16 * dc + 8 * g);
+      const int r = 32 * t + lr;
+      const half8 a = *reinterpret_cast<const half8*>(ks + swz<D>(r, 2 * dc + g));
       s[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[dc], s[t], 0, 0, 0);
     }
   }
 
-  if (MASK) {
+  // Masked keys (past the end of the sequence, or after the query when
+  // causal) get logit -inf; only tiles crossing the diagonal or the end need it.
+  if (mask) {
 #pragma unroll
     for (int t = 0; t < C::NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
         const bool ok = key < N && (!CAUSAL || key <= qrow);
-        if (!ok) s[t][r] = -INFINITY;
+        s[t][r] = ok ? s[t][r] : -INFINITY;
       }
   }
 
@@ -188,9 +178,9 @@ __device__ __forceinline__ void tile_step(const _Float16* __restrict__ ks,
   for (int t = 0; t < C::NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = xlane_max(mx);
   // Raw row max -> log2 units; a row with every key of this tile masked keeps m.
-  const float m_tile = (MASK && mx == -INFINITY) ? -INFINITY : mx * c;
+  const float m_tile = mx == -INFINITY ? -INFINITY : mx * c;
   const float m_new = fmaxf(m_run, m_tile);
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // exp2(-inf) = 0 on the first tile
   m_run = m_new;
@@ -201,31 +191,54 @@ __device__ __forceinline__ void tile_step(const _Float16* __restrict__ ks,
   for (int t = 0; t < C::NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      // exp2(-inf) = 0 for masked keys (the explicit select keeps scale = 0 exact).
       float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_new));
-      if (MASK) p = (s[t][r] == -INFINITY) ? 0.f : p;
+      if (mask) p = (s[t][r] == -INFINITY) ? 0.f : p;
       lsum += p;
       pf[t][r >> 3][r & 7] = static_cast<_Float16>(p);
     }
   l_run = l_run * alpha + lsum;
+  if (!__all(alpha == 1.0f)) {
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
+    for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
+  }
 
+  // A operand of O^T += V^T P^T: dims 32*dt + lane%32, keys of slot group g.
+  const int m16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);  // dim offset inside a 32-dim tile
 #pragma unroll
   for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      const int key0 = 32 * t + 16 * h + 4 * g + (m16 >> 2);
+      const int key1 = key0 + 8;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const half8 a =
-            *reinterpret_cast<const half8*>(vts + (32 * dt + lr) * C::VS + 32 * t + 16 * h + 8 * g);
+        const int dim = 32 * dt + dsub;
+        const short4v lo = tr_read(vs + swz<D>(key0, dim >> 3) + (dim & 7) * 2);
+        const short4v hi = tr_read(vs + swz<D>(key1, dim >> 3) + (dim & 7) * 2);
+        const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[t][h], oacc[dt], 0, 0, 0);
       }
+    }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
+__device__ __forceinline__ void compute_tile(const char* ks, const char* vs, const half8 (&qf)[Cfg<D>::DC],
+                                             f32x16 (&oacc)[Cfg<D>::DT], float& m_run, float& l_run,
+                                             float c, int kv0, int N, int qw0, int qrow, int lane) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) _Float16 smem[2 * C::BUF_ELEMS];
+  if (qw0 >= N) return;                                   // every row of this wave is padding
+  if (CAUSAL && kv0 > qw0 + kWaveRows - 1) return;        // tile above the wave's diagonal
+  const bool need_mask = (kv0 + C::BN > N) || (CAUSAL && kv0 + C::BN - 1 > qw0);
+  tile_step<D, CAUSAL>(ks, vs, qf, oacc, m_run, l_run, c, kv0, N, qrow, lane, need_mask);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_fwd_kernel(Params p) {
+  using C = Cfg<D>;
+  // Two stages of (K tile, V tile).
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
 
   // Workgroup id -> (batch*head, query tile), contiguous per XCD.
   const int nb = gridDim.x, bid = blockIdx.x;
@@ -241,13 +254,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
   const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
   const size_t kvoff = ((size_t)b * p.Hkv + kvh) * (size_t)N * D;
   const _Float16* __restrict__ qb = p.q + qoff;
-  const _Float16* __restrict__ kb = p.k + kvoff;
-  const _Float16* __restrict__ vb = p.v + kvoff;
+  const int head_bytes = N * D * 2;  // < 2^32 by the library's size limit
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvoff), (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvoff), (short)0, head_bytes, kBufferWord3);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 31, g = lane >> 5;
   const int qw0 = q0 + kWaveRows * w;  // first query row of this wave
   const int qrow = qw0 + lr;           // query row of this lane
+
+  const int kv_tiles = (N + C::BN - 1) / C::BN;
+  int nt = kv_tiles;
+  if (CAUSAL) {
+    const int last_q = (q0 + kBM < N ? q0 + kBM : N) - 1;
+    const int t_end = last_q / C::BN + 1;
+    nt = t_end < kv_tiles ? t_end : kv_tiles;
+  }
+
+  load_tile<D>(krs, smem, 0, tid);
+  load_tile<D>(vrs, smem + C::TILE_BYTES, 0, tid);
 
   // Q fragments (B operand of S^T): dims 16*dc + 8*g .. +7 of row qrow.
   half8 qf[C::DC];
@@ -259,52 +286,31 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
     qf[dc] = __builtin_bit_cast(half8, x);
   }
 
-  const int kv_tiles = (N + C::BN - 1) / C::BN;
-  int nt = kv_tiles;
-  if (CAUSAL) {
-    const int last_q = (q0 + kBM < N ? q0 + kBM : N) - 1;
-    const int t_end = last_q / C::BN + 1;
-    nt = t_end < kv_tiles ? t_end : kv_tiles;
-  }
-
   f32x16 oacc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  u32x4 kr[C::K_PER_THREAD];
-  u32x4 vr[4];
-  load_kv<D>(kb, vb, 0, N, tid, kr, vr);
-  store_kv<D>(smem, smem + C::K_ELEMS, tid, kr, vr);
+  wait_vm_all();
   __syncthreads();
 
-  const bool wave_live = qw0 < N;
+  // Stage j&1 holds tile j; tile j+1 is in flight while tile j is computed.
   for (int j = 0; j < nt; ++j) {
-    const int cur = j & 1;
-    const int kv0 = j * C::BN;
-    if (j + 1 < nt) load_kv<D>(kb, vb, kv0 + C::BN, N, tid, kr, vr);
-
-    const _Float16* ks = smem + cur * C::BUF_ELEMS;
-    const _Float16* vts = ks + C::K_ELEMS;
-    const bool skip = !wave_live || (CAUSAL && kv0 > qw0 + kWaveRows - 1);
-    if (!skip) {
-      const bool need_mask = (kv0 + C::BN > N) || (CAUSAL && kv0 + C::BN - 1 > qw0);
-      if (need_mask)
-        tile_step<D, true, CAUSAL>(ks, vts, qf, oacc, m_run, l_run, p.c, kv0, N, qrow, lr, g);
-      else
-        tile_step<D, false, CAUSAL>(ks, vts, qf, oacc, m_run, l_run, p.c, kv0, N, qrow, lr, g);
-    }
-
+    char* cur = smem + (j & 1) * 2 * C::TILE_BYTES;
+    char* nxt = smem + ((j + 1) & 1) * 2 * C::TILE_BYTES;
     if (j + 1 < nt) {
-      _Float16* nks = smem + (cur ^ 1) * C::BUF_ELEMS;
-      store_kv<D>(nks, nks + C::K_ELEMS, tid, kr, vr);
+      load_tile<D>(krs, nxt, (j + 1) * C::BN, tid);
+      load_tile<D>(vrs, nxt + C::TILE_BYTES, (j + 1) * C::BN, tid);
     }
+    compute_tile<D, CAUSAL>(cur, cur + C::TILE_BYTES, qf, oacc, m_run, l_run, p.c, j * C::BN, N,
+                            qw0, qrow, lane);
+    wait_vm_all();
     __syncthreads();
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (wave_live && qrow < N) {
+  const float l_tot = xlane_sum(l_run);
+  if (qrow < N) {
     const float inv = 1.0f / l_tot;
     _Float16* __restrict__ orow = p.o + qoff + (size_t)qrow * D;
 #pragma unroll
