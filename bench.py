@@ -112,6 +112,10 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain elementwise copy of this many MiB (fp16 -> fp16, "
+                         "y = -x) three times, so that hardware byte counters can be "
+                         "calibrated against a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -183,6 +187,16 @@ def main() -> int:
                       "median": round(float(np.median(kernel_ms)), 5)},
         "kernel_source_sha256_16": kernel_source_hash(),
     }
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 2
+        x = torch.ones(n, dtype=torch.float16, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"kernel": "torch.neg fp16 (elementwise)", "bytes_read": 2 * n,
+                                      "bytes_written": 2 * n, "launches": 3}
+        del x, y
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, q_np, k_np, v_np, o.cpu().numpy(), lse.cpu().numpy(),
                                     args.cpu_budget)

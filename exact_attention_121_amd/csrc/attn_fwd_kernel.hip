@@ -82,7 +82,6 @@ struct Cfg {
   static constexpr int DC = D / 16;                // 16-dim k-steps of Q.K
   static constexpr int DT = D / 32;                // 32-dim row tiles of O^T
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
-  static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;  // chunk XOR mask
   static constexpr int TILE_BYTES = BN * D * 2;    // one K (or V) tile
   static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
   static_assert(BN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
@@ -95,14 +94,26 @@ struct Params {
   _Float16* o;
   float* lse;
   int N, Hq, Hkv, group, q_tiles;
-  float c;          // |scale| * log2(e)
+  float c;          // |scale| * log2(e), or 1 when scale = 0 (Q is then zeroed): always > 0
   uint32_t q_sign;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
+  uint32_t q_keep;  // 0 when scale = 0 (every logit is then exactly 0), else all ones
 };
 
-// Byte offset of 16-byte chunk `c` of row `r` inside a swizzled tile.
+// Byte offset of 16-byte chunk `c` of row `r` inside a swizzled tile: the
+// chunk index is XORed with a function of the row's low four bits, chosen
+// (by exhaustive search over XOR-linear maps) so that both operand reads are
+// free of bank conflicts whether the LDS serves 128 or 256 bytes per clock:
+//   * K reads (ds_read_b128): 8 or 16 consecutive rows at one chunk;
+//   * V transpose reads (ds_read_b64_tr_b16): 4 consecutive keys x 4 chunks.
+// Rows of 256+ bytes use a 4-bit map; 128-byte rows (d = 64), where row
+// parity already selects the bank half, use a 3-bit map.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  return (r * Cfg<D>::CPR + (c ^ (r & Cfg<D>::SWZ))) * 16;
+  constexpr uint64_t kMap16 = 0x73d962c8fb51ea40ull;  // f(r) for r = 0..15, 4 bits each
+  constexpr uint64_t kMap8 = 0x4703652156127430ull;   // 3-bit variant for 128-byte rows
+  constexpr uint64_t map = Cfg<D>::CPR >= 16 ? kMap16 : kMap8;
+  const int f = static_cast<int>((map >> (4 * (r & 15))) & 15);
+  return (r * Cfg<D>::CPR + (c ^ f)) * 16;
 }
 
 // Queue the copy of rows kv0 .. kv0+BN-1 of one K or V head into a swizzled
@@ -115,7 +126,8 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, char* til
   for (int i = 0; i < C::LOADS; ++i) {
     const int p = i * kThreads + tid;  // destination chunk; lanes of a wave are consecutive
     const int row = p / C::CPR;
-    const int chunk = (p % C::CPR) ^ (row & C::SWZ);
+    // The chunk that belongs at position p % CPR of the swizzled row.
+    const int chunk = (swz<D>(row, p % C::CPR) >> 4) - row * C::CPR;
     const int src = ((kv0 + row) * D + chunk * 8) * 2;
     char* dst = tile + (i * kThreads + (tid & ~63)) * 16;  // wave-uniform base
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, src, 0, 0, 0);
@@ -179,9 +191,9 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ ks, const cha
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
   mx = xlane_max(mx);
-  // Raw row max -> log2 units; a row with every key of this tile masked keeps m.
-  const float m_tile = mx == -INFINITY ? -INFINITY : mx * c;
-  const float m_new = fmaxf(m_run, m_tile);
+  // Raw row max -> log2 units (c > 0); a row with every key of this tile
+  // masked has mx = -inf and keeps its m.
+  const float m_new = fmaxf(m_run, mx * c);
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // exp2(-inf) = 0 on the first tile
   m_run = m_new;
 
@@ -191,9 +203,8 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ ks, const cha
   for (int t = 0; t < C::NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      // exp2(-inf) = 0 for masked keys (the explicit select keeps scale = 0 exact).
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_new));
-      if (mask) p = (s[t][r] == -INFINITY) ? 0.f : p;
+      // Masked keys: fma(-inf, c > 0, -m) = -inf and exp2(-inf) = 0.
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_new));
       lsum += p;
       pf[t][r >> 3][r & 7] = static_cast<_Float16>(p);
     }
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_fwd_kernel(Pa
   for (int dc = 0; dc < C::DC; ++dc) {
     u32x4 x = qrow < N ? *reinterpret_cast<const u32x4*>(qb + (size_t)qrow * D + 16 * dc + 8 * g)
                        : u32x4{0u, 0u, 0u, 0u};
-    x ^= p.q_sign;
+    x = (x ^ p.q_sign) & p.q_keep;
     qf[dc] = __builtin_bit_cast(half8, x);
   }
 
@@ -350,8 +361,12 @@ int launch_forward(const LaunchArgs& a, void* stream) {
   p.group = a.Hq / a.Hkv;
   p.q_tiles = q_tiles;
   const double c = static_cast<double>(a.scale) * 1.4426950408889634;
-  p.c = static_cast<float>(c < 0 ? -c : c);
+  // The kernel needs c > 0 (a masked logit of -inf must give exp2(-inf) = 0).
+  // scale < 0 negates Q (exact in fp16); scale = 0 zeroes Q and uses c = 1,
+  // which gives every visible logit exactly 0, as scale = 0 does.
+  p.c = a.scale == 0.f ? 1.0f : static_cast<float>(c < 0 ? -c : c);
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
+  p.q_keep = a.scale == 0.f ? 0u : 0xffffffffu;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (a.d) {
