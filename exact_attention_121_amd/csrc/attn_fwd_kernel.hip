@@ -62,6 +62,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -150,105 +151,199 @@ __device__ __forceinline__ float xlane_sum(float x) {
   return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
-// One K/V tile for one wave: S^T = K Q^T, online softmax update, O^T += V^T P^T.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void tile_step(const char* __restrict__ ks, const char* __restrict__ vs,
-                                          const half8 (&qf)[Cfg<D>::DC],
-                                          f32x16 (&oacc)[Cfg<D>::DT], float& m_run,
-                                          float& l_run, float c, int kv0, int N, int qrow,
-                                          int lane, bool mask) {
+// Per-lane LDS byte offsets of the matrix operands inside a (swizzled) tile.
+// Tile rows 32*t + 16*h (K) or key groups (V) only add a constant, so every
+// operand read is one of these registers plus an immediate offset.
+template <int D>
+struct Offsets {
+  int k[Cfg<D>::DC];       // K rows lane%32 (+32 t), chunk 2 dc + lane/32
+  int v[2][Cfg<D>::DT];    // V keys 4 g + (lane%16)/4 (+8 for [1]), dims of row tile dt
+  __device__ __forceinline__ void init(int lane) {
+    using C = Cfg<D>;
+    const int lr = lane & 31, g = lane >> 5, m16 = lane & 15;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) k[dc] = swz<D>(lr, 2 * dc + g);
+    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);  // dim offset inside a 32-dim tile
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int dim = 32 * dt + dsub;
+        v[hi][dt] = swz<D>(4 * g + (m16 >> 2) + 8 * hi, dim >> 3) + (dim & 7) * 2;
+      }
+  }
+};
+
+// S^T = K Q^T for one key tile: s[t] holds keys 32 t .. 32 t + 31 (rows of
+// the 32x32 result) against the wave's 32 queries (columns).
+template <int D>
+__device__ __forceinline__ void qk_tile(const char* ks, const half8 (&qf)[Cfg<D>::DC],
+                                        const Offsets<D>& off, f32x16 (&s)[Cfg<D>::NT]) {
   using C = Cfg<D>;
-  const int lr = lane & 31, g = lane >> 5;
-  f32x16 s[C::NT];
 #pragma unroll
   for (int t = 0; t < C::NT; ++t) s[t] = f32x16{};
 #pragma unroll
-  for (int dc = 0; dc < C::DC; ++dc) {
+  for (int dc = 0; dc < C::DC; ++dc)
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
-      const int r = 32 * t + lr;
-      const half8 a = *reinterpret_cast<const half8*>(ks + swz<D>(r, 2 * dc + g));
+      const half8 a = *reinterpret_cast<const half8*>(ks + off.k[dc] + 32 * t * C::CPR * 16);
       s[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[dc], s[t], 0, 0, 0);
     }
-  }
+}
 
-  // Masked keys (past the end of the sequence, or after the query when
-  // causal) get logit -inf; only tiles crossing the diagonal or the end need it.
-  if (mask) {
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = key < N && (!CAUSAL || key <= qrow);
-        s[t][r] = ok ? s[t][r] : -INFINITY;
-      }
-  }
-
-  float mx = s[0][0];
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-  mx = xlane_max(mx);
-  // Raw row max -> log2 units (c > 0); a row with every key of this tile
-  // masked has mx = -inf and keeps its m.
-  const float m_new = fmaxf(m_run, mx * c);
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // exp2(-inf) = 0 on the first tile
-  m_run = m_new;
-
-  float lsum = 0.f;
-  half8 pf[C::NT][2];
+// Keys past the end of the sequence, or after the query when causal, get
+// logit -inf (then exp2 gives exactly 0).  Lane L holds keys
+// 32 t + 8 (r/4) + 4 (L/32) + r%4 of query row `qrow`.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[Cfg<D>::NT], int kv0, int N, int qrow, int g) {
+  using C = Cfg<D>;
 #pragma unroll
   for (int t = 0; t < C::NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      // Masked keys: fma(-inf, c > 0, -m) = -inf and exp2(-inf) = 0.
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_new));
-      lsum += p;
-      pf[t][r >> 3][r & 7] = static_cast<_Float16>(p);
+      const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+      const bool ok = key < N && (!CAUSAL || key <= qrow);
+      s[t][r] = ok ? s[t][r] : -INFINITY;
     }
-  l_run = l_run * alpha + lsum;
-  if (!__all(alpha == 1.0f)) {
+}
+
+// Row maximum of a tile's raw logits, in log2 units (c > 0).
+template <int D>
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[Cfg<D>::NT], float c) {
+  using C = Cfg<D>;
+  float mx = s[0][0];
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+    for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+  return xlane_max(mx) * c;
+}
+
+// The running maximum m is only raised when some row of the wave saw a logit
+// more than kLazy (log2 units) above it.  Probabilities are taken relative
+// to m, so they stay <= 2^kLazy (exact in fp16, no overflow in fp32) and the
+// result is the same function: every term of the numerator and of l shares
+// the same reference m, which cancels in O = sum(p v) / sum(p) and is added
+// back in LSE = m + log2 l.
+constexpr float kLazy = 8.0f;
+
+template <int D>
+__device__ __forceinline__ void raise_max(float m_tile, float& m_run, float& l_run,
+                                          f32x16 (&oacc)[Cfg<D>::DT]) {
+  using C = Cfg<D>;
+  if (__any(m_tile > m_run + kLazy)) {
+    const float m_new = fmaxf(m_run, m_tile);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+    m_run = m_new;
+    l_run *= alpha;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
   }
+}
 
-  // A operand of O^T += V^T P^T: dims 32*dt + lane%32, keys of slot group g.
-  const int m16 = lane & 15;
-  const int dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);  // dim offset inside a 32-dim tile
+// P = exp2(c S - m) rounded to fp16 (the B operand of the P.V product, in
+// the lane's own key order), with its sum added to the lane's partial l.
+template <int D>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[Cfg<D>::NT], float c, float m_run,
+                                             half8 (&pf)[Cfg<D>::NT][2], float& l_run) {
+  using C = Cfg<D>;
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r + 1], c, -m_run));
+      const half2v h{static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
+      pf[t][r >> 3][r & 7] = h[0];
+      pf[t][r >> 3][(r & 7) + 1] = h[1];
+      // Sum of the fp16 probabilities actually multiplied into V.
+      if ((r >> 1) & 1)
+        l1 = __builtin_amdgcn_fdot2(h, half2v{1.0f16, 1.0f16}, l1, false);
+      else
+        l0 = __builtin_amdgcn_fdot2(h, half2v{1.0f16, 1.0f16}, l0, false);
+    }
+  l_run += l0 + l1;
+}
+
+// O^T += V^T P^T for one key tile.  The A operand pairs B slot j of lane
+// group g with key 8 (j/4) + 4 g + j%4 (+16 h, +32 t): two transpose reads of
+// four keys each from V in its natural [key][dim] layout.
+template <int D>
+__device__ __forceinline__ void pv_tile(const char* vs, const half8 (&pf)[Cfg<D>::NT][2],
+                                        const Offsets<D>& off, f32x16 (&oacc)[Cfg<D>::DT]) {
+  using C = Cfg<D>;
 #pragma unroll
   for (int t = 0; t < C::NT; ++t)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int key0 = 32 * t + 16 * h + 4 * g + (m16 >> 2);
-      const int key1 = key0 + 8;
+      const int kb = (32 * t + 16 * h) * C::CPR * 16;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const int dim = 32 * dt + dsub;
-        const short4v lo = tr_read(vs + swz<D>(key0, dim >> 3) + (dim & 7) * 2);
-        const short4v hi = tr_read(vs + swz<D>(key1, dim >> 3) + (dim & 7) * 2);
+        const short4v lo = tr_read(vs + off.v[0][dt] + kb);
+        const short4v hi = tr_read(vs + off.v[1][dt] + kb);
         const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[t][h], oacc[dt], 0, 0, 0);
       }
     }
 }
 
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void compute_tile(const char* ks, const char* vs, const half8 (&qf)[Cfg<D>::DC],
-                                             f32x16 (&oacc)[Cfg<D>::DT], float& m_run, float& l_run,
-                                             float c, int kv0, int N, int qw0, int qrow, int lane) {
+// Per-wave state of the software pipeline.
+template <int D>
+struct WaveState {
+  half8 qf[Cfg<D>::DC];
+  f32x16 oacc[Cfg<D>::DT];
+  Offsets<D> off;
+  float m_run, l_run, c;
+  int N, qw0, qrow, g, nt_w;  // nt_w: key tiles this wave computes (0 for padding waves)
+};
+
+// LDS layout: K tiles in stages 0/1, then V tiles in stages 0/1.
+template <int D>
+__device__ __forceinline__ char* k_stage(char* smem, int st) { return smem + st * Cfg<D>::TILE_BYTES; }
+template <int D>
+__device__ __forceinline__ char* v_stage(char* smem, int st) { return smem + (2 + st) * Cfg<D>::TILE_BYTES; }
+
+// Iteration j of the pipeline ([CANN-FA] section "Concrete flow": scores,
+// online-softmax update and P.V for key block j).  On entry K_{j+1} sits in
+// K stage (j+1)&1, V_j in V stage j&1, and s_cur holds the masked logits of
+// tile j with the running max already raised for them.  The matrix cores
+// compute S_{j+1} = K_{j+1} Q^T while the vector ALUs turn s_cur into P_j;
+// then O += P_j V_j runs while the vector ALUs reduce S_{j+1}.  Meanwhile
+// V_{j+1} and K_{j+2} stream into the stages freed by the previous iteration
+// ([CANN-FA] section "Ascend C implementation": load the next block while the
+// current one is computed).
+template <int D, bool CAUSAL, int PAR>
+__device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
+                                              __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                              int tid, WaveState<D>& w, f32x16 (&s_cur)[Cfg<D>::NT],
+                                              f32x16 (&s_nxt)[Cfg<D>::NT]) {
   using C = Cfg<D>;
-  if (qw0 >= N) return;                                   // every row of this wave is padding
-  if (CAUSAL && kv0 > qw0 + kWaveRows - 1) return;        // tile above the wave's diagonal
-  const bool need_mask = (kv0 + C::BN > N) || (CAUSAL && kv0 + C::BN - 1 > qw0);
-  tile_step<D, CAUSAL>(ks, vs, qf, oacc, m_run, l_run, c, kv0, N, qrow, lane, need_mask);
+  if (j + 1 < nt) load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), (j + 1) * C::BN, tid);
+  if (j + 2 < nt) load_tile<D>(krs, k_stage<D>(smem, PAR), (j + 2) * C::BN, tid);
+  if (j < w.nt_w) {
+    // S_{j+1} is computed even past this wave's last tile (reading a stale
+    // but in-bounds stage) so that the matrix and vector work stay in one
+    // block the scheduler can interleave; it is discarded then.
+    qk_tile<D>(k_stage<D>(smem, PAR ^ 1), w.qf, w.off, s_nxt);
+    half8 pf[C::NT][2];
+    softmax_tile<D>(s_cur, w.c, w.m_run, pf, w.l_run);
+    pv_tile<D>(v_stage<D>(smem, PAR), pf, w.off, w.oacc);
+    if (j + 1 < w.nt_w) {
+      const int kv1 = (j + 1) * C::BN;
+      if (kv1 + C::BN > w.N || (CAUSAL && kv1 + C::BN - 1 > w.qw0))
+        mask_tile<D, CAUSAL>(s_nxt, kv1, w.N, w.qrow, w.g);
+      raise_max<D>(tile_max<D>(s_nxt, w.c), w.m_run, w.l_run, w.oacc);
+    }
+  }
+  wait_vm_all();
+  __syncthreads();
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
-  // Two stages of (K tile, V tile).
+  // K stages 0/1 then V stages 0/1.
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
 
   // Workgroup id -> (batch*head, query tile), contiguous per XCD.
@@ -271,10 +366,14 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_fwd_kernel(Pa
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvoff), (short)0, head_bytes, kBufferWord3);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 31, g = lane >> 5;
-  const int qw0 = q0 + kWaveRows * w;  // first query row of this wave
-  const int qrow = qw0 + lr;           // query row of this lane
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  WaveState<D> w;
+  w.N = N;
+  w.c = p.c;
+  w.g = lane >> 5;
+  w.qw0 = q0 + kWaveRows * wv;  // first query row of this wave
+  w.qrow = w.qw0 + (lane & 31);  // query row of this lane
+  w.off.init(lane);
 
   const int kv_tiles = (N + C::BN - 1) / C::BN;
   int nt = kv_tiles;
@@ -283,58 +382,65 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_fwd_kernel(Pa
     const int t_end = last_q / C::BN + 1;
     nt = t_end < kv_tiles ? t_end : kv_tiles;
   }
-
-  load_tile<D>(krs, smem, 0, tid);
-  load_tile<D>(vrs, smem + C::TILE_BYTES, 0, tid);
-
-  // Q fragments (B operand of S^T): dims 16*dc + 8*g .. +7 of row qrow.
-  half8 qf[C::DC];
-#pragma unroll
-  for (int dc = 0; dc < C::DC; ++dc) {
-    u32x4 x = qrow < N ? *reinterpret_cast<const u32x4*>(qb + (size_t)qrow * D + 16 * dc + 8 * g)
-                       : u32x4{0u, 0u, 0u, 0u};
-    x = (x ^ p.q_sign) & p.q_keep;
-    qf[dc] = __builtin_bit_cast(half8, x);
+  if (w.qw0 >= N) {
+    w.nt_w = 0;  // every row of this wave is padding
+  } else if (CAUSAL) {
+    const int last_w = (w.qw0 + kWaveRows < N ? w.qw0 + kWaveRows : N) - 1;
+    w.nt_w = last_w / C::BN + 1;
+  } else {
+    w.nt_w = nt;
   }
 
-  f32x16 oacc[C::DT];
+  load_tile<D>(krs, k_stage<D>(smem, 0), 0, tid);
+  load_tile<D>(vrs, v_stage<D>(smem, 0), 0, tid);
+  if (nt > 1) load_tile<D>(krs, k_stage<D>(smem, 1), C::BN, tid);
+
+  // Q fragments (B operand of S^T): dims 16*dc + 8*g .. +7 of row qrow.
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dc = 0; dc < C::DC; ++dc) {
+    u32x4 x = w.qrow < N ? *reinterpret_cast<const u32x4*>(qb + (size_t)w.qrow * D + 16 * dc + 8 * w.g)
+                         : u32x4{0u, 0u, 0u, 0u};
+    x = (x ^ p.q_sign) & p.q_keep;
+    w.qf[dc] = __builtin_bit_cast(half8, x);
+  }
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) w.oacc[dt] = f32x16{};
+  w.m_run = -INFINITY;
+  w.l_run = 0.f;
 
   wait_vm_all();
   __syncthreads();
 
-  // Stage j&1 holds tile j; tile j+1 is in flight while tile j is computed.
-  for (int j = 0; j < nt; ++j) {
-    char* cur = smem + (j & 1) * 2 * C::TILE_BYTES;
-    char* nxt = smem + ((j + 1) & 1) * 2 * C::TILE_BYTES;
-    if (j + 1 < nt) {
-      load_tile<D>(krs, nxt, (j + 1) * C::BN, tid);
-      load_tile<D>(vrs, nxt + C::TILE_BYTES, (j + 1) * C::BN, tid);
-    }
-    compute_tile<D, CAUSAL>(cur, cur + C::TILE_BYTES, qf, oacc, m_run, l_run, p.c, j * C::BN, N,
-                            qw0, qrow, lane);
-    wait_vm_all();
-    __syncthreads();
+  // Prologue: logits of tile 0 and the first running max.
+  f32x16 sa[C::NT], sb[C::NT];
+  if (w.nt_w > 0) {
+    qk_tile<D>(k_stage<D>(smem, 0), w.qf, w.off, sa);
+    if (C::BN > N || (CAUSAL && C::BN - 1 > w.qw0)) mask_tile<D, CAUSAL>(sa, 0, N, w.qrow, w.g);
+    // Key 0 is visible to every row, so this max is finite.
+    w.m_run = tile_max<D>(sa, w.c);
+  }
+
+  for (int j = 0; j < nt; j += 2) {
+    pipeline_step<D, CAUSAL, 0>(j, nt, smem, krs, vrs, tid, w, sa, sb);
+    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1>(j + 1, nt, smem, krs, vrs, tid, w, sb, sa);
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
-  const float l_tot = xlane_sum(l_run);
-  if (qrow < N) {
+  const float l_tot = xlane_sum(w.l_run);
+  if (w.qrow < N) {
     const float inv = 1.0f / l_tot;
-    _Float16* __restrict__ orow = p.o + qoff + (size_t)qrow * D;
+    _Float16* __restrict__ orow = p.o + qoff + (size_t)w.qrow * D;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         half4 h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(oacc[dt][4 * rq + i] * inv);
-        *reinterpret_cast<half4*>(orow + 32 * dt + 8 * rq + 4 * g) = h;
+        for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(w.oacc[dt][4 * rq + i] * inv);
+        *reinterpret_cast<half4*>(orow + 32 * dt + 8 * rq + 4 * w.g) = h;
       }
-    if (p.lse != nullptr && g == 0)
-      p.lse[((size_t)b * p.Hq + hq) * N + qrow] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+    if (p.lse != nullptr && w.g == 0)
+      p.lse[((size_t)b * p.Hq + hq) * N + w.qrow] = (w.m_run + __builtin_log2f(l_tot)) * kLn2;
   }
 }
 
