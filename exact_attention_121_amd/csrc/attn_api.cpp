@@ -14,6 +14,7 @@
 namespace {
 
 constexpr int64_t kLimit31 = int64_t{1} << 31;
+constexpr int64_t kLimitHead = int64_t{1} << 30;  // elements per head
 constexpr int64_t kRowsPerBlock = 128;  // query rows per workgroup
 
 // [a, a + na) and [b, b + nb) share a byte (empty ranges never overlap).
@@ -36,13 +37,14 @@ extern "C" int attn_check_args(const void* q, const void* k, const void* v, cons
   if (B == 0 || N == 0) return ATTN_OK;  // empty problem: nothing to touch
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARG;
 
-  // 32-bit index limits of the kernel.
-  if (N >= kLimit31 / d) return ATTN_ERR_INVALID_ARG;  // N * d < 2^31
+  // 32-bit index limits of the kernel: one K/V head spans at most 2^31 bytes
+  // (N * d <= 2^30), so a byte offset at or above 2^31 is always outside it.
+  if (N > kLimitHead / d) return ATTN_ERR_INVALID_ARG;
   const int64_t q_tiles = (N + kRowsPerBlock - 1) / kRowsPerBlock;
   if (Hq >= kLimit31 || B >= kLimit31 / Hq) return ATTN_ERR_INVALID_ARG;
   if (B * Hq >= kLimit31 / q_tiles) return ATTN_ERR_INVALID_ARG;  // grid < 2^31
 
-  // B * Hq < 2^31 and N * d < 2^31, so these byte counts fit in int64.
+  // B * Hq < 2^31 and N * d <= 2^30, so these byte counts fit in int64.
   const int64_t q_bytes = B * Hq * N * d * 2;
   const int64_t kv_bytes = B * Hkv * N * d * 2;
   const int64_t lse_bytes = B * Hq * N * 4;

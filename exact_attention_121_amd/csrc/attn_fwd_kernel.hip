@@ -70,14 +70,34 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
 constexpr int kThreads = 256;  // 4 waves of 64 lanes
-constexpr int kWaveRows = 32;  // query rows per wave
-constexpr int kBM = 128;       // query rows per workgroup
+constexpr int kWaves = kThreads / 64;
 constexpr float kLn2 = 0.69314718055994531f;
 // Buffer resource word 3 for raw (unformatted, stride 0) buffer access on gfx9-family parts.
 constexpr int kBufferWord3 = 0x00020000;
 
+// Query blocks of 32 rows per wave, per head_dim.  Two blocks per wave let
+// every K/V operand read from LDS feed two matrix instructions and halve the
+// K/V traffic per query row (the workgroup covers 256 rows); that needs more
+// than 256 registers per lane, so those kernels run one wave per SIMD.
+#ifndef ATTN_QB64
+#define ATTN_QB64 1
+#endif
+#ifndef ATTN_QB128
+#define ATTN_QB128 1
+#endif
+#ifndef ATTN_QB256
+#define ATTN_QB256 1
+#endif
+template <int D>
+constexpr int query_blocks() {
+  return D == 64 ? ATTN_QB64 : (D == 128 ? ATTN_QB128 : ATTN_QB256);
+}
+
 template <int D>
 struct Cfg {
+  static constexpr int QB = query_blocks<D>();     // 32-row query blocks per wave
+  static constexpr int WAVE_ROWS = 32 * QB;        // query rows per wave
+  static constexpr int BM = kWaves * WAVE_ROWS;    // query rows per workgroup
   static constexpr int BN = (D == 256) ? 32 : 64;  // keys per K/V tile
   static constexpr int NT = BN / 32;               // 32-key sub-tiles of S^T
   static constexpr int DC = D / 16;                // 16-dim k-steps of Q.K
@@ -85,6 +105,8 @@ struct Cfg {
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * D * 2;    // one K (or V) tile
   static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
+  // Workgroups per CU the register budget allows.
+  static constexpr int WG_PER_CU = (QB == 1 && D != 256) ? 2 : 1;
   static_assert(BN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
@@ -117,22 +139,49 @@ __device__ __forceinline__ int swz(int r, int c) {
   return (r * Cfg<D>::CPR + (c ^ f)) * 16;
 }
 
-// Queue the copy of rows kv0 .. kv0+BN-1 of one K or V head into a swizzled
-// LDS tile.  Rows at or past N read as zeros (buffer range check).
+// Byte offsets, relative to a tile's first row, of the 16-byte chunks that
+// thread `tid` copies into a swizzled tile (the chunk that belongs at
+// position p % CPR of row p / CPR of the tile).
 template <int D>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, char* tile, int kv0,
-                                          int tid) {
+struct LoadOffsets {
+  uint32_t src[Cfg<D>::LOADS];
+  __device__ __forceinline__ void init(int tid) {
+    using C = Cfg<D>;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int p = i * kThreads + tid;  // destination chunk; lanes of a wave are consecutive
+      const int row = p / C::CPR;
+      const int chunk = (swz<D>(row, p % C::CPR) >> 4) - row * C::CPR;
+      src[i] = static_cast<uint32_t>((row * D + chunk * 8) * 2);
+    }
+  }
+};
+
+// A tile base at or above 2^31 bytes lies outside every K/V head (a head is
+// at most 2^31 bytes), so each read of the tile fails the buffer range check:
+// no memory is touched and the stage receives zeros.  Used for tiles past
+// the end of the loop, so that the load instructions need no branch.
+constexpr uint32_t kSkipTile = 0x80000000u;
+
+// Queue the copy of the tile whose first row starts at byte `base` of one K
+// or V head into a swizzled LDS tile.  Rows at or past N read as zeros
+// (buffer range check).
+template <int D>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, char* tile, uint32_t base,
+                                          const LoadOffsets<D>& lo, int tid) {
   using C = Cfg<D>;
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
-    const int p = i * kThreads + tid;  // destination chunk; lanes of a wave are consecutive
-    const int row = p / C::CPR;
-    // The chunk that belongs at position p % CPR of the swizzled row.
-    const int chunk = (swz<D>(row, p % C::CPR) >> 4) - row * C::CPR;
-    const int src = ((kv0 + row) * D + chunk * 8) * 2;
     char* dst = tile + (i * kThreads + (tid & ~63)) * 16;  // wave-uniform base
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, src, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, static_cast<int>(base + lo.src[i]),
+                                             0, 0, 0);
   }
+}
+
+// Byte offset of the first row of key tile j inside a head, or kSkipTile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_base(int j, int nt) {
+  return j < nt ? static_cast<uint32_t>(j) * (Cfg<D>::BN * D * 2) : kSkipTile;
 }
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -174,49 +223,68 @@ struct Offsets {
   }
 };
 
-// S^T = K Q^T for one key tile: s[t] holds keys 32 t .. 32 t + 31 (rows of
-// the 32x32 result) against the wave's 32 queries (columns).
 template <int D>
-__device__ __forceinline__ void qk_tile(const char* ks, const half8 (&qf)[Cfg<D>::DC],
-                                        const Offsets<D>& off, f32x16 (&s)[Cfg<D>::NT]) {
+using STile = f32x16[Cfg<D>::QB][Cfg<D>::NT];  // logits of one key tile, per query block
+template <int D>
+using PTile = half8[Cfg<D>::QB][Cfg<D>::NT][2];  // fp16 probabilities of one key tile
+template <int D>
+using OAcc = f32x16[Cfg<D>::QB][Cfg<D>::DT];  // output accumulators O^T
+template <int D>
+using QFrag = half8[Cfg<D>::QB][Cfg<D>::DC];  // Q rows as B operands
+
+// S^T = K Q^T for one key tile: s[qb][t] holds keys 32 t .. 32 t + 31 (rows
+// of the 32x32 result) against query block qb (columns).  Each K operand
+// read from LDS serves every query block of the wave.
+template <int D>
+__device__ __forceinline__ void qk_tile(const char* ks, const QFrag<D>& qf, const Offsets<D>& off,
+                                        STile<D>& s) {
   using C = Cfg<D>;
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t) s[t] = f32x16{};
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) s[qb][t] = f32x16{};
 #pragma unroll
   for (int dc = 0; dc < C::DC; ++dc)
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       const half8 a = *reinterpret_cast<const half8*>(ks + off.k[dc] + 32 * t * C::CPR * 16);
-      s[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[dc], s[t], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+        s[qb][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[qb][dc], s[qb][t], 0, 0, 0);
     }
 }
 
 // Keys past the end of the sequence, or after the query when causal, get
 // logit -inf (then exp2 gives exactly 0).  Lane L holds keys
-// 32 t + 8 (r/4) + 4 (L/32) + r%4 of query row `qrow`.
+// 32 t + 8 (r/4) + 4 (L/32) + r%4 of query row `qrow` (+32 per block).
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[Cfg<D>::NT], int kv0, int N, int qrow, int g) {
+__device__ __forceinline__ void mask_tile(STile<D>& s, int kv0, int N, int qrow, int g) {
   using C = Cfg<D>;
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t)
+  for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-      const bool ok = key < N && (!CAUSAL || key <= qrow);
-      s[t][r] = ok ? s[t][r] : -INFINITY;
-    }
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = key < N && (!CAUSAL || key <= qrow + 32 * qb);
+        s[qb][t][r] = ok ? s[qb][t][r] : -INFINITY;
+      }
 }
 
-// Row maximum of a tile's raw logits, in log2 units (c > 0).
+// Row maxima of a tile's raw logits, in log2 units (c > 0).
 template <int D>
-__device__ __forceinline__ float tile_max(const f32x16 (&s)[Cfg<D>::NT], float c) {
+__device__ __forceinline__ void tile_max(const STile<D>& s, float c, float (&m)[Cfg<D>::QB]) {
   using C = Cfg<D>;
-  float mx = s[0][0];
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t)
+  for (int qb = 0; qb < C::QB; ++qb) {
+    float mx = s[qb][0][0];
 #pragma unroll
-    for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-  return xlane_max(mx) * c;
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[qb][t][r]);
+    m[qb] = xlane_max(mx) * c;
+  }
 }
 
 // The running maximum m is only raised when some row of the wave saw a logit
@@ -228,50 +296,68 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[Cfg<D>::NT], float c
 constexpr float kLazy = 8.0f;
 
 template <int D>
-__device__ __forceinline__ void raise_max(float m_tile, float& m_run, float& l_run,
-                                          f32x16 (&oacc)[Cfg<D>::DT]) {
+__device__ __forceinline__ void raise_max(const float (&m_tile)[Cfg<D>::QB], float (&m_run)[Cfg<D>::QB],
+                                          float (&l_run)[Cfg<D>::QB], OAcc<D>& oacc) {
   using C = Cfg<D>;
-  if (__any(m_tile > m_run + kLazy)) {
-    const float m_new = fmaxf(m_run, m_tile);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
-    m_run = m_new;
-    l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
+  for (int qb = 0; qb < C::QB; ++qb) {
+    if (__any(m_tile[qb] > m_run[qb] + kLazy)) {
+      const float m_new = fmaxf(m_run[qb], m_tile[qb]);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // 0 while m_run = -inf
+      m_run[qb] = m_new;
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) oacc[qb][dt] *= alpha;
+    }
   }
 }
 
-// P = exp2(c S - m) rounded to fp16 (the B operand of the P.V product, in
-// the lane's own key order), with its sum added to the lane's partial l.
+// P = exp2(c S - m) rounded to fp16: the B operand of the P.V product, in
+// the lane's own key order.
 template <int D>
-__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[Cfg<D>::NT], float c, float m_run,
-                                             half8 (&pf)[Cfg<D>::NT][2], float& l_run) {
+__device__ __forceinline__ void softmax_tile(const STile<D>& s, float c, const float (&m_run)[Cfg<D>::QB],
+                                             PTile<D>& pf) {
   using C = Cfg<D>;
-  float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t)
+  for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], c, -m_run));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r + 1], c, -m_run));
-      const half2v h{static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
-      pf[t][r >> 3][r & 7] = h[0];
-      pf[t][r >> 3][(r & 7) + 1] = h[1];
-      // Sum of the fp16 probabilities actually multiplied into V.
-      if ((r >> 1) & 1)
-        l1 = __builtin_amdgcn_fdot2(h, half2v{1.0f16, 1.0f16}, l1, false);
-      else
-        l0 = __builtin_amdgcn_fdot2(h, half2v{1.0f16, 1.0f16}, l0, false);
-    }
-  l_run += l0 + l1;
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pf[qb][t][r >> 3][r & 7] =
+            static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][t][r], c, -m_run[qb])));
+}
+
+// Adds the sum of the fp16 probabilities (exactly the values multiplied
+// into V) to the lane's partial row sums l.
+template <int D>
+__device__ __forceinline__ void add_row_sums(const PTile<D>& pf, float (&l_run)[Cfg<D>::QB]) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+      {
+        const half8 x = pf[qb][t][h];
+        l0 = __builtin_amdgcn_fdot2(half2v{x[0], x[1]}, half2v{1.0f16, 1.0f16}, l0, false);
+        l1 = __builtin_amdgcn_fdot2(half2v{x[2], x[3]}, half2v{1.0f16, 1.0f16}, l1, false);
+        l0 = __builtin_amdgcn_fdot2(half2v{x[4], x[5]}, half2v{1.0f16, 1.0f16}, l0, false);
+        l1 = __builtin_amdgcn_fdot2(half2v{x[6], x[7]}, half2v{1.0f16, 1.0f16}, l1, false);
+      }
+    l_run[qb] += l0 + l1;
+  }
 }
 
 // O^T += V^T P^T for one key tile.  The A operand pairs B slot j of lane
 // group g with key 8 (j/4) + 4 g + j%4 (+16 h, +32 t): two transpose reads of
-// four keys each from V in its natural [key][dim] layout.
+// four keys each from V in its natural [key][dim] layout, shared by every
+// query block of the wave.
 template <int D>
-__device__ __forceinline__ void pv_tile(const char* vs, const half8 (&pf)[Cfg<D>::NT][2],
-                                        const Offsets<D>& off, f32x16 (&oacc)[Cfg<D>::DT]) {
+__device__ __forceinline__ void pv_tile(const char* vs, const PTile<D>& pf, const Offsets<D>& off,
+                                        OAcc<D>& oacc) {
   using C = Cfg<D>;
 #pragma unroll
   for (int t = 0; t < C::NT; ++t)
@@ -283,7 +369,9 @@ __device__ __forceinline__ void pv_tile(const char* vs, const half8 (&pf)[Cfg<D>
         const short4v lo = tr_read(vs + off.v[0][dt] + kb);
         const short4v hi = tr_read(vs + off.v[1][dt] + kb);
         const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[t][h], oacc[dt], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb)
+          oacc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[qb][t][h], oacc[qb][dt], 0, 0, 0);
       }
     }
 }
@@ -291,11 +379,12 @@ __device__ __forceinline__ void pv_tile(const char* vs, const half8 (&pf)[Cfg<D>
 // Per-wave state of the software pipeline.
 template <int D>
 struct WaveState {
-  half8 qf[Cfg<D>::DC];
-  f32x16 oacc[Cfg<D>::DT];
+  QFrag<D> qf;
+  OAcc<D> oacc;
   Offsets<D> off;
-  float m_run, l_run, c;
-  int N, qw0, qrow, g, nt_w;  // nt_w: key tiles this wave computes (0 for padding waves)
+  float m_run[Cfg<D>::QB], l_run[Cfg<D>::QB];
+  float c;
+  int N, qw0, qrow, g, nt_w;  // qrow: row of this lane in block 0; nt_w: key tiles this wave computes
 };
 
 // LDS layout: K tiles in stages 0/1, then V tiles in stages 0/1.
@@ -303,6 +392,10 @@ template <int D>
 __device__ __forceinline__ char* k_stage(char* smem, int st) { return smem + st * Cfg<D>::TILE_BYTES; }
 template <int D>
 __device__ __forceinline__ char* v_stage(char* smem, int st) { return smem + (2 + st) * Cfg<D>::TILE_BYTES; }
+
+// Instruction groups for the compiler's scheduler (masks of
+// __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
 
 // Iteration j of the pipeline ([CANN-FA] section "Concrete flow": scores,
 // online-softmax update and P.V for key block j).  On entry K_{j+1} sits in
@@ -316,32 +409,78 @@ __device__ __forceinline__ char* v_stage(char* smem, int st) { return smem + (2 
 template <int D, bool CAUSAL, int PAR>
 __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                              int tid, WaveState<D>& w, f32x16 (&s_cur)[Cfg<D>::NT],
-                                              f32x16 (&s_nxt)[Cfg<D>::NT]) {
+                                              const LoadOffsets<D>& lo, int tid, WaveState<D>& w,
+                                              STile<D>& s_cur, STile<D>& s_nxt) {
   using C = Cfg<D>;
-  if (j + 1 < nt) load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), (j + 1) * C::BN, tid);
-  if (j + 2 < nt) load_tile<D>(krs, k_stage<D>(smem, PAR), (j + 2) * C::BN, tid);
+  const uint32_t v_base = tile_base<D>(j + 1, nt);
+  const uint32_t k_base = tile_base<D>(j + 2, nt);
   if (j < w.nt_w) {
+    load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), v_base, lo, tid);
+    load_tile<D>(krs, k_stage<D>(smem, PAR), k_base, lo, tid);
     // S_{j+1} is computed even past this wave's last tile (reading a stale
     // but in-bounds stage) so that the matrix and vector work stay in one
     // block the scheduler can interleave; it is discarded then.
     qk_tile<D>(k_stage<D>(smem, PAR ^ 1), w.qf, w.off, s_nxt);
-    half8 pf[C::NT][2];
-    softmax_tile<D>(s_cur, w.c, w.m_run, pf, w.l_run);
-    pv_tile<D>(v_stage<D>(smem, PAR), pf, w.off, w.oacc);
-    if (j + 1 < w.nt_w) {
-      const int kv1 = (j + 1) * C::BN;
-      if (kv1 + C::BN > w.N || (CAUSAL && kv1 + C::BN - 1 > w.qw0))
-        mask_tile<D, CAUSAL>(s_nxt, kv1, w.N, w.qrow, w.g);
-      raise_max<D>(tile_max<D>(s_nxt, w.c), w.m_run, w.l_run, w.oacc);
+    PTile<D> pf;
+    softmax_tile<D>(s_cur, w.c, w.m_run, pf);
+    // Materialise P_j here, so that the compiler keeps the softmax next to
+    // the S_{j+1} product instead of sinking it past the mask branch.
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(pf[qb][t][h]));
+    if constexpr (C::DC >= 8) {
+      // One MFMA of S_{j+1}, then a share of the softmax of tile j; a K
+      // operand read per group of query blocks; the V/K copies ride along.
+      // (With d = 64 the compiler's own order measured faster.)
+      constexpr int kMfma = C::DC * C::NT * C::QB;
+      constexpr int kValu = (3 * 16 * C::NT * C::QB + kMfma - 1) / kMfma;
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+#pragma unroll
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, kValu, 0);
+        if (i % C::QB == C::QB - 1) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        if (i < 2 * C::LOADS) __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+      }
     }
+    const int kv1 = (j + 1) * C::BN;
+    if (kv1 + C::BN > w.N || (CAUSAL && kv1 + C::BN - 1 > w.qw0))
+      mask_tile<D, CAUSAL>(s_nxt, kv1, w.N, w.qrow, w.g);
+    // Raised issue priority while this wave feeds the matrix cores with
+    // P_j V_j, so that the other wave of the SIMD fills the gaps with its
+    // vector work rather than the reverse.
+    __builtin_amdgcn_s_setprio(1);
+    pv_tile<D>(v_stage<D>(smem, PAR), pf, w.off, w.oacc);
+    add_row_sums<D>(pf, w.l_run);
+    float m_tile[C::QB];
+    tile_max<D>(s_nxt, w.c, m_tile);
+    if constexpr (C::DC >= 8) {
+      // One MFMA of P_j V_j, then V operand reads and a share of the
+      // row-max reduction of S_{j+1}.
+      constexpr int kMfma = C::NT * 2 * C::DT * C::QB;
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        if (i % C::QB == C::QB - 1) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 2, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (j + 1 < w.nt_w) raise_max<D>(m_tile, w.m_run, w.l_run, w.oacc);
+  } else {
+    load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), v_base, lo, tid);
+    load_tile<D>(krs, k_stage<D>(smem, PAR), k_base, lo, tid);
   }
   wait_vm_all();
   __syncthreads();
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
   // K stages 0/1 then V stages 0/1.
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
@@ -355,12 +494,14 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_fwd_kernel(Pa
   if (CAUSAL) qt = p.q_tiles - 1 - qt;
   const int b = bh / p.Hq, hq = bh - b * p.Hq, kvh = hq / p.group;
   const int N = p.N;
-  const int q0 = qt * kBM;
+  const int q0 = qt * C::BM;
 
   const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
   const size_t kvoff = ((size_t)b * p.Hkv + kvh) * (size_t)N * D;
-  const _Float16* __restrict__ qb = p.q + qoff;
-  const int head_bytes = N * D * 2;  // < 2^32 by the library's size limit
+  const _Float16* __restrict__ qb_ptr = p.q + qoff;
+  // Bytes of one K/V head: <= 2^31 by the library's size limit; the range
+  // field holds it as an unsigned 32-bit count.
+  const int head_bytes = static_cast<int>(static_cast<uint32_t>(N) * (D * 2));
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvoff), (short)0, head_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -371,82 +512,95 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void attn_fwd_kernel(Pa
   w.N = N;
   w.c = p.c;
   w.g = lane >> 5;
-  w.qw0 = q0 + kWaveRows * wv;  // first query row of this wave
-  w.qrow = w.qw0 + (lane & 31);  // query row of this lane
+  w.qw0 = q0 + C::WAVE_ROWS * wv;  // first query row of this wave
+  w.qrow = w.qw0 + (lane & 31);    // query row of this lane in block 0
   w.off.init(lane);
 
   const int kv_tiles = (N + C::BN - 1) / C::BN;
   int nt = kv_tiles;
   if (CAUSAL) {
-    const int last_q = (q0 + kBM < N ? q0 + kBM : N) - 1;
+    const int last_q = (q0 + C::BM < N ? q0 + C::BM : N) - 1;
     const int t_end = last_q / C::BN + 1;
     nt = t_end < kv_tiles ? t_end : kv_tiles;
   }
   if (w.qw0 >= N) {
     w.nt_w = 0;  // every row of this wave is padding
   } else if (CAUSAL) {
-    const int last_w = (w.qw0 + kWaveRows < N ? w.qw0 + kWaveRows : N) - 1;
+    const int last_w = (w.qw0 + C::WAVE_ROWS < N ? w.qw0 + C::WAVE_ROWS : N) - 1;
     w.nt_w = last_w / C::BN + 1;
   } else {
     w.nt_w = nt;
   }
 
-  load_tile<D>(krs, k_stage<D>(smem, 0), 0, tid);
-  load_tile<D>(vrs, v_stage<D>(smem, 0), 0, tid);
-  if (nt > 1) load_tile<D>(krs, k_stage<D>(smem, 1), C::BN, tid);
+  LoadOffsets<D> lo;
+  lo.init(tid);
+  load_tile<D>(krs, k_stage<D>(smem, 0), 0, lo, tid);
+  load_tile<D>(vrs, v_stage<D>(smem, 0), 0, lo, tid);
+  load_tile<D>(krs, k_stage<D>(smem, 1), tile_base<D>(1, nt), lo, tid);
 
-  // Q fragments (B operand of S^T): dims 16*dc + 8*g .. +7 of row qrow.
+  // Q fragments (B operand of S^T): dims 16*dc + 8*g .. +7 of each row.
 #pragma unroll
-  for (int dc = 0; dc < C::DC; ++dc) {
-    u32x4 x = w.qrow < N ? *reinterpret_cast<const u32x4*>(qb + (size_t)w.qrow * D + 16 * dc + 8 * w.g)
-                         : u32x4{0u, 0u, 0u, 0u};
-    x = (x ^ p.q_sign) & p.q_keep;
-    w.qf[dc] = __builtin_bit_cast(half8, x);
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int row = w.qrow + 32 * qb;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
+      u32x4 x = row < N ? *reinterpret_cast<const u32x4*>(qb_ptr + (size_t)row * D + 16 * dc + 8 * w.g)
+                        : u32x4{0u, 0u, 0u, 0u};
+      x = (x ^ p.q_sign) & p.q_keep;
+      w.qf[qb][dc] = __builtin_bit_cast(half8, x);
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) w.oacc[qb][dt] = f32x16{};
+    w.m_run[qb] = -INFINITY;
+    w.l_run[qb] = 0.f;
   }
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) w.oacc[dt] = f32x16{};
-  w.m_run = -INFINITY;
-  w.l_run = 0.f;
 
   wait_vm_all();
   __syncthreads();
 
   // Prologue: logits of tile 0 and the first running max.
-  f32x16 sa[C::NT], sb[C::NT];
+  STile<D> sa, sb;
   if (w.nt_w > 0) {
     qk_tile<D>(k_stage<D>(smem, 0), w.qf, w.off, sa);
     if (C::BN > N || (CAUSAL && C::BN - 1 > w.qw0)) mask_tile<D, CAUSAL>(sa, 0, N, w.qrow, w.g);
-    // Key 0 is visible to every row, so this max is finite.
-    w.m_run = tile_max<D>(sa, w.c);
+    // Key 0 is visible to every row, so these maxima are finite.
+    tile_max<D>(sa, w.c, w.m_run);
   }
+  // Iteration 0 refills K stage 0: every wave must be done reading K_0.
+  __syncthreads();
 
   for (int j = 0; j < nt; j += 2) {
-    pipeline_step<D, CAUSAL, 0>(j, nt, smem, krs, vrs, tid, w, sa, sb);
-    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1>(j + 1, nt, smem, krs, vrs, tid, w, sb, sa);
+    pipeline_step<D, CAUSAL, 0>(j, nt, smem, krs, vrs, lo, tid, w, sa, sb);
+    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1>(j + 1, nt, smem, krs, vrs, lo, tid, w, sb, sa);
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
-  const float l_tot = xlane_sum(w.l_run);
-  if (w.qrow < N) {
-    const float inv = 1.0f / l_tot;
-    _Float16* __restrict__ orow = p.o + qoff + (size_t)w.qrow * D;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int row = w.qrow + 32 * qb;
+    const float l_tot = xlane_sum(w.l_run[qb]);
+    if (row < N) {
+      const float inv = 1.0f / l_tot;
+      _Float16* __restrict__ orow = p.o + qoff + (size_t)row * D;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        half4 h;
+      for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(w.oacc[dt][4 * rq + i] * inv);
-        *reinterpret_cast<half4*>(orow + 32 * dt + 8 * rq + 4 * w.g) = h;
-      }
-    if (p.lse != nullptr && w.g == 0)
-      p.lse[((size_t)b * p.Hq + hq) * N + w.qrow] = (w.m_run + __builtin_log2f(l_tot)) * kLn2;
+        for (int rq = 0; rq < 4; ++rq) {
+          half4 h;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(w.oacc[qb][dt][4 * rq + i] * inv);
+          *reinterpret_cast<half4*>(orow + 32 * dt + 8 * rq + 4 * w.g) = h;
+        }
+      if (p.lse != nullptr && w.g == 0)
+        p.lse[((size_t)b * p.Hq + hq) * N + row] = (w.m_run[qb] + __builtin_log2f(l_tot)) * kLn2;
+    }
   }
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_t(const LaunchArgs& a, const Params& p, int q_tiles, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>(a.B) * a.Hq * q_tiles;
+hipError_t launch_t(const LaunchArgs& a, Params p, hipStream_t s) {
+  p.q_tiles = (a.N + Cfg<D>::BM - 1) / Cfg<D>::BM;
+  const unsigned grid = static_cast<unsigned>(a.B) * a.Hq * p.q_tiles;
   hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
@@ -454,7 +608,6 @@ hipError_t launch_t(const LaunchArgs& a, const Params& p, int q_tiles, hipStream
 }  // namespace
 
 int launch_forward(const LaunchArgs& a, void* stream) {
-  const int q_tiles = (a.N + kBM - 1) / kBM;
   Params p;
   p.q = static_cast<const _Float16*>(a.q);
   p.k = static_cast<const _Float16*>(a.k);
@@ -465,7 +618,6 @@ int launch_forward(const LaunchArgs& a, void* stream) {
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.group = a.Hq / a.Hkv;
-  p.q_tiles = q_tiles;
   const double c = static_cast<double>(a.scale) * 1.4426950408889634;
   // The kernel needs c > 0 (a masked logit of -inf must give exp2(-inf) = 0).
   // scale < 0 negates Q (exact in fp16); scale = 0 zeroes Q and uses c = 1,
@@ -477,13 +629,13 @@ int launch_forward(const LaunchArgs& a, void* stream) {
   hipError_t e;
   switch (a.d) {
     case 64:
-      e = a.causal ? launch_t<64, true>(a, p, q_tiles, s) : launch_t<64, false>(a, p, q_tiles, s);
+      e = a.causal ? launch_t<64, true>(a, p, s) : launch_t<64, false>(a, p, s);
       break;
     case 128:
-      e = a.causal ? launch_t<128, true>(a, p, q_tiles, s) : launch_t<128, false>(a, p, q_tiles, s);
+      e = a.causal ? launch_t<128, true>(a, p, s) : launch_t<128, false>(a, p, s);
       break;
     case 256:
-      e = a.causal ? launch_t<256, true>(a, p, q_tiles, s) : launch_t<256, false>(a, p, q_tiles, s);
+      e = a.causal ? launch_t<256, true>(a, p, s) : launch_t<256, false>(a, p, s);
       break;
     default:
       e = hipErrorInvalidValue;

@@ -8,7 +8,7 @@
 namespace attn {
 
 // Arguments after validation: every size fits the kernel's 32-bit index math
-// (N * d < 2^31, B * Hq * ceil(N / 128) < 2^31) and d is 64, 128 or 256.
+// (N * d <= 2^30, B * Hq * ceil(N / 128) < 2^31) and d is 64, 128 or 256.
 struct LaunchArgs {
   const void* q;
   const void* k;

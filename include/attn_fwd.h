@@ -84,7 +84,7 @@ enum attn_status {
  *   causal 0 or non-zero
  *   stream HIP stream to queue the kernel on (NULL = default stream)
  *
- * Limits: N * d < 2^31 and B * Hq * ceil(N / 128) < 2^31.  The output o (and
+ * Limits: N * d <= 2^30 and B * Hq * ceil(N / 128) < 2^31.  The output o (and
  * lse) must not overlap q, k, v or each other.
  * Returns an attn_status value.
  */

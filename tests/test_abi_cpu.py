@@ -66,6 +66,10 @@ def test_valid_arguments():
     for d in (64, 128, 256):
         assert check(d=d) == ea.ATTN_OK
     assert check(Hq=8, Hkv=8) == ea.ATTN_OK and check(Hq=8, Hkv=1) == ea.ATTN_OK
+    # The largest head the kernel addresses: N * d = 2^30 elements (2 GiB).
+    far = 1 << 44
+    assert check(B=1, Hq=1, Hkv=1, N=(1 << 30) // 128, q=far, k=2 * far, v=3 * far, o=4 * far,
+                 lse=5 * far) == ea.ATTN_OK
 
 
 def test_empty_problems_are_ok_without_pointers():
@@ -78,7 +82,7 @@ def test_empty_problems_are_ok_without_pointers():
     dict(B=-1), dict(N=-3), dict(Hq=0), dict(Hkv=0), dict(Hq=-8), dict(d=0), dict(d=-64),
     dict(Hq=8, Hkv=3), dict(Hq=2, Hkv=4),
     dict(scale=float("inf")), dict(scale=float("-inf")), dict(scale=float("nan")),
-    dict(N=(1 << 31) // 128), dict(N=1 << 40),                 # N * d >= 2^31
+    dict(N=(1 << 30) // 128 + 1), dict(N=1 << 40),             # N * d > 2^30
     dict(B=1 << 20, Hq=1 << 12, Hkv=1, N=128),                  # grid >= 2^31
     dict(o=P + 64),                                             # o overlaps q
     dict(o=2 * P + 4096),                                       # o overlaps k
