@@ -507,7 +507,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_fwd_kernel(P
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvoff), (short)0, head_bytes, kBufferWord3);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   WaveState<D> w;
   w.N = N;
   w.c = p.c;
