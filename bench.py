@@ -31,10 +31,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank lines removed, so
+    that only a change of the code itself invalidates the stored counters."""
+    import re
+
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
@@ -47,7 +55,7 @@ def measured_traffic(workload_name: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload_name)
-    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not entry or entry.get("kernel_code_sha256_16") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -185,7 +193,7 @@ def main() -> int:
                      "traffic": traffic},
         "kernel_ms": {"mean": round(avg_kernel_ms, 5), "min": round(float(np.min(kernel_ms)), 5),
                       "median": round(float(np.median(kernel_ms)), 5)},
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_code_sha256_16": kernel_source_hash(),
     }
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 2

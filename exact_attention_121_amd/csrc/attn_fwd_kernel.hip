@@ -38,13 +38,19 @@
 //     from V kept in its natural [key][dim] layout.
 //   * K and V tiles move from device memory straight into LDS with
 //     buffer_load_dwordx4 ... lds (no register staging; reads past the end of
-//     the sequence return zeros), double-buffered: tile j+1 is in flight while
-//     tile j is computed ([CANN-FA] section "Ascend C implementation": load
-//     block j+1 while block j is computed so that data movement hides behind
-//     the matrix unit).  16-byte chunks are XOR-swizzled by row so that the
-//     matrix-operand reads hit distinct LDS banks.
-//   * exp is exp2 with scale*log2(e) folded into one fused multiply-add; the
-//     O rescale is skipped when no row of the wave raised its maximum.
+//     the sequence return zeros), double-buffered per operand: K_{j+1} and
+//     V_j are resident while V_{j+1} and K_{j+2} are in flight ([CANN-FA]
+//     section "Ascend C implementation": load block j+1 while block j is
+//     computed so that data movement hides behind the matrix unit).  16-byte
+//     chunks are XOR-swizzled by row so that the matrix-operand reads hit
+//     distinct LDS banks.
+//   * Software pipeline per wave: iteration j computes S_{j+1} = K_{j+1} Q^T
+//     on the matrix cores interleaved with the softmax of tile j on the
+//     vector ALUs, then O += P_j V_j interleaved with the row max of S_{j+1}.
+//   * exp is exp2 with scale*log2(e) folded into one fused multiply-add.  The
+//     running max is raised lazily (only when a row's new logits exceed it by
+//     more than 8 in log2 units), so the O rescale is rare and probabilities
+//     stay <= 256; row sums add the fp16 probabilities with v_dot2.
 //   * Causal: key tiles entirely above a wave's diagonal are skipped; only
 //     tiles crossing the diagonal or the end of the sequence are masked.
 //   * Workgroup ids are remapped so that each of the 8 XCDs (each with its
