@@ -113,6 +113,9 @@ struct Cfg {
   static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
   // Workgroups per CU the register budget allows.
   static constexpr int WG_PER_CU = (QB == 1 && D != 256) ? 2 : 1;
+  // Matrix operands read from LDS ahead of their MFMA (K reads; twice as
+  // many V transpose reads, two per MFMA); measured on gfx950.
+  static constexpr int K_AHEAD = D == 256 ? 6 : 4;
   static_assert(BN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
@@ -443,7 +446,7 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
       // (With d = 64 the compiler's own order measured faster.)
       constexpr int kMfma = C::DC * C::NT * C::QB;
       constexpr int kValu = (3 * 16 * C::NT * C::QB + kMfma - 1) / kMfma;
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, C::K_AHEAD, 0);
 #pragma unroll
       for (int i = 0; i < kMfma; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
@@ -467,7 +470,7 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
       // One MFMA of P_j V_j, then V operand reads and a share of the
       // row-max reduction of S_{j+1}.
       constexpr int kMfma = C::NT * 2 * C::DT * C::QB;
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * C::K_AHEAD, 0);
 #pragma unroll
       for (int i = 0; i < kMfma; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
