@@ -18,10 +18,13 @@ from .binding import (  # noqa: F401
     AttnError,
     AttnUnsupportedError,
     attn_check_args,
+    attn_check_decode_args,
+    attn_decode,
+    attn_decode_workspace_size,
     attn_fwd,
     attn_status_string,
     attn_version,
     load_library,
 )
 
-__version__ = "0.1.0"
+__version__ = "0.2.0"

@@ -21,7 +21,8 @@ ATTN_ERR_INVALID_ARG = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_DEVICE = 3
 
-EXPORTS = ("attn_fwd", "attn_check_args", "attn_status_string", "attn_version")
+EXPORTS = ("attn_fwd", "attn_check_args", "attn_decode", "attn_decode_workspace_size",
+           "attn_check_decode_args", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -30,7 +31,7 @@ class AttnError(RuntimeError):
     """A non-zero status from the library."""
 
     def __init__(self, status: int, message: str):
-        super().__init__(f"attn_fwd status {status}: {message}")
+        super().__init__(f"attn status {status}: {message}")
         self.status = status
 
 
@@ -59,6 +60,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float]
     lib.attn_check_args.restype = ctypes.c_int
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                ctypes.c_int, vp, i64, vp]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
+    lib.attn_decode_workspace_size.restype = ctypes.c_int
+    lib.attn_check_decode_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                           ctypes.c_float, vp, i64]
+    lib.attn_check_decode_args.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -142,5 +151,77 @@ def attn_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, out=N
             q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
             out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
             B, Hq, Hkv, N, d, float(scale), 1 if causal else 0, s.cuda_stream or None)
+    _raise_for(status)
+    return out, lse
+
+
+def attn_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d) -> int:
+    """Workspace bytes attn_decode needs for this shape (host only)."""
+    out = ctypes.c_int64(0)
+    _raise_for(load_library().attn_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, ctypes.byref(out)))
+    return out.value
+
+
+def attn_check_decode_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, workspace, workspace_bytes) -> int:
+    """Host-only validation of attn_decode (pointers as integers or None); returns a status."""
+    return load_library().attn_check_decode_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                                 workspace, workspace_bytes)
+
+
+def attn_decode(q, k, v, *, scale: float | None = None, causal: bool = True, out=None, lse=None,
+                return_lse: bool = True, workspace=None, stream=None):
+    """Decode step on torch fp16 tensors: q [B, Hq, Nq, d] are the last Nq
+    positions of a sequence whose keys/values k, v [B, Hkv, Nk, d] are
+    cached (Nq <= Nk).  With causal, query i sees keys 0 .. Nk - Nq + i.
+    ``workspace`` is an optional uint8 device tensor of at least
+    attn_decode_workspace_size(...) bytes (allocated here when omitted).
+    Returns (o, lse) like attn_fwd.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be torch.float16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on an AMD GPU (torch 'cuda' device), got {t.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
+    B, Hq, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != torch.float16 or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous fp16 tensor shaped like q on q's device")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32
+                              or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq] on q's device")
+    need = attn_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = lib.attn_decode(
+            q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
+            out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
+            B, Hq, Hkv, Nq, Nk, d, float(scale), 1 if causal else 0,
+            workspace.data_ptr() or None, ws_bytes, s.cuda_stream or None)
     _raise_for(status)
     return out, lse

@@ -25,6 +25,14 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return pa < pb + static_cast<uintptr_t>(nb) && pb < pa + static_cast<uintptr_t>(na);
 }
 
+// The kernels move Q, K, V, O and the decode workspace in 16-byte vectors
+// and the LSE as 4-byte words.
+bool misaligned(const void* p, uintptr_t align) { return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0; }
+
+bool misaligned_tensors(const void* q, const void* k, const void* v, const void* o, const float* lse) {
+  return misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4);
+}
+
 }  // namespace
 
 extern "C" int attn_check_args(const void* q, const void* k, const void* v, const void* o,
@@ -36,6 +44,7 @@ extern "C" int attn_check_args(const void* q, const void* k, const void* v, cons
   if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || N == 0) return ATTN_OK;  // empty problem: nothing to touch
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (misaligned_tensors(q, k, v, o, lse)) return ATTN_ERR_INVALID_ARG;
 
   // 32-bit index limits of the kernel: one K/V head spans at most 2^31 bytes
   // (N * d <= 2^30), so a byte offset at or above 2^31 is always outside it.
@@ -80,6 +89,88 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   return attn::launch_forward(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
+namespace {
+
+// Shape rules of the decode entry points (no pointer is looked at).
+int check_decode_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale) {
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (Nq > Nk) return ATTN_ERR_INVALID_ARG;  // the queries are the last Nq of Nk positions
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  if (Nk > kLimitHead / d) return ATTN_ERR_INVALID_ARG;
+  if (Hq >= kLimit31 || B >= kLimit31 / Hq || B * Hq >= kLimit31 / Nq) return ATTN_ERR_INVALID_ARG;
+  const attn::DecodePlan plan = attn::decode_plan(B, Hq, Hkv, Nq, Nk, d);
+  if (B * Hkv * plan.row_blocks >= kLimit31 / plan.splits) return ATTN_ERR_INVALID_ARG;  // grid < 2^31
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                                          int64_t d, int64_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  const int st = check_decode_shape(B, Hq, Hkv, Nq, Nk, d, 1.0f);
+  if (st != ATTN_OK) return st;
+  *bytes = (B == 0 || Nq == 0) ? 0 : attn::decode_plan(B, Hq, Hkv, Nq, Nk, d).workspace_bytes;
+  return ATTN_OK;
+}
+
+extern "C" int attn_check_decode_args(const void* q, const void* k, const void* v, const void* o,
+                                      const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                                      int64_t Nk, int64_t d, float scale, const void* workspace,
+                                      int64_t workspace_bytes) {
+  const int st = check_decode_shape(B, Hq, Hkv, Nq, Nk, d, scale);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || Nq == 0) return ATTN_OK;  // empty problem: nothing to touch
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || workspace == nullptr)
+    return ATTN_ERR_INVALID_ARG;
+  if (misaligned_tensors(q, k, v, o, lse) || misaligned(workspace, 16)) return ATTN_ERR_INVALID_ARG;
+  const int64_t need = attn::decode_plan(B, Hq, Hkv, Nq, Nk, d).workspace_bytes;
+  if (workspace_bytes < need) return ATTN_ERR_INVALID_ARG;
+  const int64_t q_bytes = B * Hq * Nq * d * 2;
+  const int64_t kv_bytes = B * Hkv * Nk * d * 2;
+  const int64_t lse_bytes = B * Hq * Nq * 4;
+  const void* ins[3] = {q, k, v};
+  const int64_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(o, q_bytes, ins[i], in_bytes[i])) return ATTN_ERR_INVALID_ARG;
+    if (overlaps(workspace, need, ins[i], in_bytes[i])) return ATTN_ERR_INVALID_ARG;
+    if (lse != nullptr && overlaps(lse, lse_bytes, ins[i], in_bytes[i])) return ATTN_ERR_INVALID_ARG;
+  }
+  if (overlaps(workspace, need, o, q_bytes)) return ATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && (overlaps(lse, lse_bytes, o, q_bytes) || overlaps(lse, lse_bytes, workspace, need)))
+    return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                           int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                           void* workspace, int64_t workspace_bytes, struct ihipStream_t* stream) {
+  const int st = attn_check_decode_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, workspace,
+                                        workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  attn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.B = static_cast<int>(B);
+  a.Hq = static_cast<int>(Hq);
+  a.Hkv = static_cast<int>(Hkv);
+  a.Nq = static_cast<int>(Nq);
+  a.Nk = static_cast<int>(Nk);
+  a.d = static_cast<int>(d);
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.plan = attn::decode_plan(B, Hq, Hkv, Nq, Nk, d);
+  return attn::launch_decode(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
 extern "C" const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK:
@@ -95,4 +186,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" const char* attn_version(void) { return "attn_fwd 0.1.0 gfx950"; }
+extern "C" const char* attn_version(void) { return "attn_fwd 0.2.0 gfx950"; }

@@ -24,6 +24,55 @@ struct LaunchArgs {
 // HIP runtime's status of the launch (0 = hipSuccess).
 int launch_forward(const LaunchArgs& a, void* stream);
 
+// Decode (KV cache) work plan: Nq new queries per query head against Nk
+// cached keys.  The G = Hq / Hkv query heads of a key/value head are packed
+// into rows r = g * Nq + i (row blocks of kDecodeRows); the keys are split
+// into `splits` chunks of `chunk_tiles` key tiles, each chunk handled by one
+// workgroup that writes a partial O and LSE to the workspace; a second
+// kernel merges the partials.  Shared by the validation (workspace size) and
+// the launcher so both see the same plan.
+constexpr int64_t kDecodeRows = 128;          // packed rows per workgroup
+constexpr int64_t kDecodeTargetGroups = 1024;  // enough workgroups to fill the chip
+
+struct DecodePlan {
+  int64_t row_blocks, kv_tiles, splits, chunk_tiles;
+  int64_t workspace_bytes;  // partial O (fp32) and LSE (fp32) of every split
+};
+
+inline int64_t decode_key_tile(int64_t d) { return d == 256 ? 32 : 64; }
+
+inline DecodePlan decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
+  DecodePlan p;
+  const int64_t rows = (Hq / Hkv) * Nq;
+  p.row_blocks = (rows + kDecodeRows - 1) / kDecodeRows;
+  const int64_t bn = decode_key_tile(d);
+  p.kv_tiles = (Nk + bn - 1) / bn;
+  const int64_t groups = B * Hkv * p.row_blocks;
+  int64_t s = (kDecodeTargetGroups + groups - 1) / groups;
+  if (s > p.kv_tiles) s = p.kv_tiles;
+  if (s < 1) s = 1;
+  p.chunk_tiles = (p.kv_tiles + s - 1) / s;
+  p.splits = (p.kv_tiles + p.chunk_tiles - 1) / p.chunk_tiles;  // no empty chunk
+  p.workspace_bytes = groups * p.splits * kDecodeRows * (d + 1) * 4;
+  return p;
+}
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  void* workspace;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  DecodePlan plan;
+};
+
+// Queues the split kernel and the merge kernel on `stream`.
+int launch_decode(const DecodeArgs& a, void* stream);
+
 }  // namespace attn
 
 #endif  // ATTN_LAUNCH_H_

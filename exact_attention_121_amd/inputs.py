@@ -16,6 +16,9 @@ Recipe (every draw uses numpy's PCG64 ``default_rng``):
     are {0, N-1} plus R-2 distinct rows drawn uniformly without replacement
     from 1..N-2 by ``default_rng(seed + 10**6 + b*Hq + hq)``, sorted.
 
+  * Decode inputs: Q [B, Hq, Nq, d] is drawn first, then K and V
+    [B, Hkv, Nk, d], each as above (one head at a time, N(0, sigma^2)).
+
 The workloads mirror the shapes the pages measure or show: the LLaMA-7B layer
 (seq 2048, 32 heads, head_dim 128, fp16) of the FlashAttention operator page
 on www.mooersco.com (section on the gap to standard attention), its
@@ -23,7 +26,10 @@ on www.mooersco.com (section on the gap to standard attention), its
 hwcomputing.csdn.net tutorial's measurement table, and the GQA/MQA and
 128K-context statements of the gitcode.csdn.net page (section 6).  There are
 no model weights or activations here, so N(0, sigma^2) values stand in for
-them at the same shapes.
+them at the same shapes.  The decode workloads put one (or a few) new
+queries against a cache of those lengths and head layouts; the batched one
+is sized so that its cache (2 GiB) is several times the chip's last-level
+cache, so that it measures HBM.
 """
 
 from __future__ import annotations
@@ -139,3 +145,55 @@ def sample_rows(w: Workload, count: int | None = None, seed: int | None = None) 
             inner = rng.choice(np.arange(1, N - 1), size=R - 2, replace=False)
             out[b, hq] = np.sort(np.concatenate([[0, N - 1], inner]))
     return out
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq new queries (the last Nq positions) against a cache of Nk keys/values."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool = True
+    sigma: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def hbm_bytes(self) -> int:
+        """Algorithmic bytes: K and V read once, Q read once, O (fp16) and LSE (fp32) written once."""
+        kv = 2 * self.B * self.Hkv * self.Nk * self.d * 2
+        q_o = 2 * self.B * self.Hq * self.Nq * self.d * 2
+        return kv + q_o + self.B * self.Hq * self.Nq * 4
+
+    def describe(self) -> str:
+        mask = "causal" if self.causal else "non-causal"
+        return f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} Nq={self.Nq} Nk={self.Nk} d={self.d} {mask}"
+
+
+DECODE_WORKLOADS = {
+    1: DecodeWorkload("gqa_decode_batch64", 64, 32, 8, 1, 8192, 128, seed=2001),
+    2: DecodeWorkload("long_context_mqa_decode", 1, 32, 1, 1, 131072, 128, sigma=0.5, seed=2002),
+    3: DecodeWorkload("gqa_d256_decode", 1, 32, 8, 1, 8192, 256, seed=2003),
+    4: DecodeWorkload("multi_query_decode", 4, 32, 8, 16, 8192, 128, seed=2004),
+}
+
+
+def make_decode_qkv(B, Hq, Hkv, Nq, Nk, d, seed, sigma=1.0):
+    """Q [B,Hq,Nq,d], K/V [B,Hkv,Nk,d] as fp16 numpy arrays, per the recipe."""
+    rng = np.random.default_rng(seed)
+    q = _draw(rng, B, Hq, Nq, d, sigma, 0.0, 1.0)
+    k = _draw(rng, B, Hkv, Nk, d, sigma, 0.0, 1.0)
+    v = _draw(rng, B, Hkv, Nk, d, sigma, 0.0, 1.0)
+    return q, k, v
+
+
+def make_decode_inputs(w: DecodeWorkload, seed: int | None = None):
+    s = w.seed if seed is None else seed
+    return make_decode_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, s, w.sigma)

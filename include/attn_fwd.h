@@ -61,8 +61,9 @@ struct ihipStream_t;
 
 enum attn_status {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, bad grouping, non-finite
-                               scale, overlapping output, size over limits */
+  ATTN_ERR_INVALID_ARG = 1, /* NULL or misaligned pointer, bad size, bad grouping,
+                               non-finite scale, overlapping output, size over
+                               limits, workspace too small */
   ATTN_ERR_UNSUPPORTED = 2, /* head_dim not in {64, 128, 256} */
   ATTN_ERR_DEVICE = 3       /* the HIP runtime refused the launch */
 };
@@ -85,7 +86,8 @@ enum attn_status {
  *   stream HIP stream to queue the kernel on (NULL = default stream)
  *
  * Limits: N * d <= 2^30 and B * Hq * ceil(N / 128) < 2^31.  The output o (and
- * lse) must not overlap q, k, v or each other.
+ * lse) must not overlap q, k, v or each other.  q, k, v and o must be 16-byte
+ * aligned and lse 4-byte aligned (ATTN_ERR_INVALID_ARG otherwise).
  * Returns an attn_status value.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -102,10 +104,64 @@ int attn_check_args(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, int64_t B, int64_t Hq, int64_t Hkv,
                     int64_t N, int64_t d, float scale);
 
+/*
+ * Decode (KV cache): Nq new queries per query head against Nk cached keys.
+ *
+ * The computation is the same definition as attn_fwd ([CANN-FA] section
+ * "Where is the bottleneck of standard attention"), for queries that are the
+ * last Nq positions of an Nk-long sequence: query i sits at position
+ * Nk - Nq + i, so with causal != 0 it sees keys 0 .. Nk - Nq + i (with
+ * Nq == Nk this is attn_fwd's causal mask).  GQA/MQA ([FA-Infer] section 6)
+ * is what makes this path cheap: the G = Hq / Hkv query heads of a key/value
+ * head are computed together, so each cached K/V byte is read once.
+ *
+ *   q      [B][Hq][Nq][d]  fp16, read only
+ *   k, v   [B][Hkv][Nk][d] fp16, read only (the cache)
+ *   o      [B][Hq][Nq][d]  fp16, written: every element exactly once
+ *   lse    [B][Hq][Nq]     fp32 natural log, or NULL
+ *   B, Nq  >= 0 (0 is an empty problem: ATTN_OK, nothing touched);
+ *          1 <= Nq <= Nk otherwise
+ *   Hq, Hkv, d, scale, causal, stream: as for attn_fwd
+ *   workspace, workspace_bytes: caller-owned device memory of at least
+ *          attn_decode_workspace_size(...) bytes, used for the per-chunk
+ *          partial results; its contents on entry do not matter and on
+ *          return are unspecified.  It must be 16-byte aligned, must not
+ *          overlap any other buffer, and two calls in flight must not share
+ *          it.  Pointer alignment as for attn_fwd.
+ *
+ * Two kernels are queued on `stream` (the per-chunk pass, then the merge);
+ * the call never synchronises.  Limits: Nk * d <= 2^30 and
+ * B * Hq * Nq < 2^31.  Returns an attn_status value; on any status other
+ * than ATTN_OK nothing has been launched.
+ */
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                int64_t d, float scale, int causal, void* workspace,
+                int64_t workspace_bytes, struct ihipStream_t* stream);
+
+/*
+ * attn_decode_workspace_size - bytes of workspace attn_decode needs for this
+ * shape (0 for an empty problem), written to *bytes.  Host only.  Returns
+ * ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED for shapes attn_decode would
+ * reject, and ATTN_ERR_INVALID_ARG when bytes is NULL.
+ */
+int attn_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                               int64_t Nk, int64_t d, int64_t* bytes);
+
+/*
+ * attn_check_decode_args - the argument validation of attn_decode on the
+ * host only (pointers compared, never dereferenced; no HIP call).
+ */
+int attn_check_decode_args(const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, int64_t B,
+                           int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                           int64_t d, float scale, const void* workspace,
+                           int64_t workspace_bytes);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Static version string of the library, e.g. "attn_fwd 0.1.0 gfx950". */
+/* Static version string of the library, e.g. "attn_fwd 0.2.0 gfx950". */
 const char* attn_version(void);
 
 #ifdef __cplusplus

@@ -8,7 +8,8 @@ binding) never imports, calls or links it, and the two share no code.
 Modules
 -------
 attention  plain two-pass fp64 attention (numpy), the reference every GPU
-           result is compared with, plus the online-softmax recurrence in the
+           result is compared with (also for decode steps, where the queries
+           are the last positions of the cached sequence), plus the online-softmax recurrence in the
            pages' own step order (used only to pin the two-pass form).
 brute      the textbook softmax definition written as scalar loops over
            mpmath numbers, with no max-subtraction, for tiny inputs.
@@ -27,6 +28,7 @@ against closed forms, invariants, brute force and mutation tests; none is
 """
 
 from .attention import (  # noqa: F401
+    attention_decode_ref,
     attention_ref,
     attention_probs,
     online_attention,

@@ -159,6 +159,48 @@ def attention_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     return O, LSE
 
 
+def attention_decode_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                         causal: bool = True):
+    """Two-pass fp64 attention for a decode (KV-cache) step.
+
+    q: [B, Hq, Nq, d] are the last Nq positions of a sequence whose keys and
+    values k, v: [B, Hkv, Nk, d] (Nq <= Nk) cover all Nk positions.  Same
+    definition as ``attention_ref`` ([CANN-FA] section "Where is the
+    bottleneck of standard attention"; [FA-Infer] section 2); the only new
+    reading is where the queries sit: query i is position Nk - Nq + i, so
+    with ``causal`` it sees keys j <= Nk - Nq + i (with Nq == Nk this is the
+    causal mask of ``attention_ref``).  GQA/MQA grouping as ``kv_head_of``
+    ([FA-Infer] section 6, which ties GQA/MQA to the KV cache of inference).
+    Returns (O [B, Hq, Nq, d] fp64, LSE [B, Hq, Nq] fp64).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape[:3] != (B, Hkv, Nk) or Nq > Nk:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    sigma = _fp32_scale(scale)
+    pos = (Nk - Nq) + np.arange(Nq)          # position of each query in the sequence
+    keys = np.arange(Nk)
+    O = np.empty((B, Hq, Nq, v.shape[3]), dtype=np.float64)
+    LSE = np.empty((B, Hq, Nq), dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            kvh = kv_head_of(hq, Hq, Hkv)
+            K = k[b, kvh].astype(np.float64)
+            V = v[b, kvh].astype(np.float64)
+            S = sigma * (q[b, hq].astype(np.float64) @ K.T)    # [Nq, Nk]
+            if causal:
+                S = np.where(keys[None, :] <= pos[:, None], S, -np.inf)
+            m = S.max(axis=1)                                  # pass 1
+            E = np.exp(S - m[:, None])                         # pass 2
+            l = E.sum(axis=1)
+            O[b, hq] = (E / l[:, None]) @ V
+            LSE[b, hq] = m + np.log(l)
+    return O, LSE
+
+
 def online_attention(q, k, v, scale, causal=False, blocks=None,
                      normalise_each_step=True, num=float, exp=math.exp,
                      log=math.log):

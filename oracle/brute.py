@@ -21,17 +21,20 @@ import numpy as np
 
 
 def attention_brute(q, k, v, scale, causal=False, dps=50):
-    """O and LSE for q [B,Hq,N,d], k/v [B,Hkv,N,d] as nested lists of mpf.
+    """O and LSE for q [B,Hq,Nq,d], k/v [B,Hkv,N,d] as nested lists of mpf.
 
     Every input element is converted exactly (binary floats are exact in
     mpmath).  The scale is taken as the fp32 number the library boundary
-    receives.  Query i sees key j iff (not causal) or j <= i.
+    receives.  The Nq queries are the last Nq of the N positions (Nq = N for
+    ordinary attention): query i sees key j iff (not causal) or
+    j <= N - Nq + i.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Nq, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    shift = N - Nq
     G = Hq // Hkv
     with mpmath.workdps(dps):
         sigma = mpmath.mpf(float(np.float32(scale)))
@@ -42,10 +45,10 @@ def attention_brute(q, k, v, scale, causal=False, dps=50):
             for h in range(Hq):
                 g = h // G
                 Oh, Lh = [], []
-                for i in range(N):
+                for i in range(Nq):
                     weights = []
                     for j in range(N):
-                        if causal and j > i:
+                        if causal and j > shift + i:
                             continue
                         dot = mpmath.mpf(0)
                         for c in range(d):

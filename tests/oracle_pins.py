@@ -416,6 +416,67 @@ def pin_torch_sdpa(impl):
         _close(O, ref, 1e-12, 1e-13, f"sdpa {Hq}/{Hkv} causal={causal}")
 
 
+def pin_decode_is_last_rows(impl):
+    """A decode step equals the last Nq rows of full attention over the whole
+    sequence (the queries placed at the last positions, any values in the
+    other rows), causal or not, with GQA/MQA grouping."""
+    rng = _rng(21)
+    for B, Hq, Hkv, Nq, Nk in ((1, 1, 1, 1, 9), (2, 4, 2, 3, 17), (1, 6, 1, 5, 5), (2, 8, 2, 16, 40)):
+        d = 6
+        qd = _rand(rng, B, Hq, Nq, d)
+        k, v = _rand(rng, B, Hkv, Nk, d), _rand(rng, B, Hkv, Nk, d)
+        qfull = _rand(rng, B, Hq, Nk, d)
+        qfull[:, :, Nk - Nq:] = qd
+        rows = np.arange(Nk - Nq, Nk)
+        for causal in (False, True):
+            O, L = impl.attention_decode_ref(qd, k, v, 0.6, causal=causal)
+            Of, Lf = impl.attention_ref(qfull, k, v, 0.6, causal=causal, rows=rows)
+            _close(O, Of, 1e-13, 1e-14, f"decode vs last rows Nq={Nq} Nk={Nk} causal={causal}")
+            _close(L, Lf, 1e-13, 1e-13, f"decode LSE vs last rows Nq={Nq} Nk={Nk} causal={causal}")
+
+
+def pin_decode_brute_force(impl):
+    """Decode against the textbook softmax in mpmath (no max subtraction)."""
+    rng = _rng(22)
+    for Hq, Hkv, Nq, Nk in ((1, 1, 1, 4), (2, 1, 2, 5), (4, 2, 3, 6)):
+        q = _rand(rng, 1, Hq, Nq, 3)
+        k, v = _rand(rng, 1, Hkv, Nk, 3), _rand(rng, 1, Hkv, Nk, 2)
+        for causal in (False, True):
+            O, L = impl.attention_decode_ref(q, k, v, 0.8, causal=causal)
+            Ob, Lb = attention_brute(q, k, v, 0.8, causal=causal)
+            _close(O, to_float_array(Ob), 1e-13, 1e-14, f"decode brute Nq={Nq} causal={causal}")
+            _close(L, to_float_array(Lb), 1e-13, 1e-14, f"decode brute LSE Nq={Nq} causal={causal}")
+
+
+def pin_decode_scale_zero_prefix_means(impl):
+    """Scale 0: every visible logit is 0, so decode query i (position
+    Nk - Nq + i) averages the values of keys 0 .. Nk - Nq + i and its LSE is
+    ln(Nk - Nq + i + 1); non-causal, every query averages all Nk values."""
+    rng = _rng(23)
+    Nq, Nk = 4, 11
+    q, k, v = _rand(rng, 1, 2, Nq, 5), _rand(rng, 1, 1, Nk, 5), _rand(rng, 1, 1, Nk, 5)
+    O, L = impl.attention_decode_ref(q, k, v, 0.0, causal=True)
+    for i in range(Nq):
+        cnt = Nk - Nq + i + 1
+        for h in range(2):
+            _close(O[0, h, i], v[0, 0, :cnt].mean(axis=0), 1e-14, 1e-15, f"prefix mean row {i}")
+            _close(L[0, h, i], np.log(cnt), 1e-15, 1e-15, f"ln count row {i}")
+    O, L = impl.attention_decode_ref(q, k, v, 0.0, causal=False)
+    _close(O[0, 0], np.broadcast_to(v[0, 0].mean(axis=0), (Nq, 5)), 1e-14, 1e-15, "non-causal mean")
+    _close(L, np.full((1, 2, Nq), np.log(Nk)), 1e-15, 1e-15, "ln Nk")
+
+
+def pin_decode_full_length(impl):
+    """With Nq == Nk a decode step is ordinary attention."""
+    rng = _rng(24)
+    q, k, v = _rand(rng, 2, 4, 9, 5), _rand(rng, 2, 2, 9, 5), _rand(rng, 2, 2, 9, 5)
+    for causal in (False, True):
+        O, L = impl.attention_decode_ref(q, k, v, 0.3, causal=causal)
+        Of, Lf = impl.attention_ref(q, k, v, 0.3, causal=causal)
+        _close(O, Of, 1e-14, 1e-15, f"Nq == Nk causal={causal}")
+        _close(L, Lf, 1e-14, 1e-15, f"Nq == Nk LSE causal={causal}")
+
+
 ALL_PINS = [
     pin_golden_closed_forms,
     pin_scale_zero,
@@ -433,4 +494,8 @@ ALL_PINS = [
     pin_online_block_invariance,
     pin_brute_force_small,
     pin_torch_sdpa,
+    pin_decode_is_last_rows,
+    pin_decode_brute_force,
+    pin_decode_scale_zero_prefix_means,
+    pin_decode_full_length,
 ]

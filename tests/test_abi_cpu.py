@@ -66,6 +66,7 @@ def test_valid_arguments():
     for d in (64, 128, 256):
         assert check(d=d) == ea.ATTN_OK
     assert check(Hq=8, Hkv=8) == ea.ATTN_OK and check(Hq=8, Hkv=1) == ea.ATTN_OK
+    assert check(q=P + 16, o=4 * P + 48, lse=5 * P + 4) == ea.ATTN_OK   # 16- and 4-byte alignment suffice
     # The largest head the kernel addresses: N * d = 2^30 elements (2 GiB).
     far = 1 << 44
     assert check(B=1, Hq=1, Hkv=1, N=(1 << 30) // 128, q=far, k=2 * far, v=3 * far, o=4 * far,
@@ -88,6 +89,7 @@ def test_empty_problems_are_ok_without_pointers():
     dict(o=2 * P + 4096),                                       # o overlaps k
     dict(lse=4 * P + 2),                                        # lse overlaps o
     dict(lse=3 * P),                                            # lse overlaps v
+    dict(q=P + 2), dict(k=2 * P + 8), dict(v=3 * P + 4), dict(o=4 * P + 1), dict(lse=5 * P + 2),  # alignment
 ])
 def test_invalid_arguments(over):
     assert check(**over) == ea.ATTN_ERR_INVALID_ARG, over
@@ -119,3 +121,127 @@ def test_binding_refuses_cpu_tensors():
         ea.attn_fwd(q, q, q)
     with pytest.raises(TypeError):
         ea.attn_fwd(q.float(), q, q)
+
+
+# --- decode (KV-cache) entry points -----------------------------------------
+
+DGOOD = dict(q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, B=2, Hq=8, Hkv=2, Nq=4, Nk=1000, d=128, scale=0.125,
+             workspace=6 * P, workspace_bytes=None)
+
+
+def dcheck(**over):
+    a = dict(DGOOD, **over)
+    if a["workspace_bytes"] is None:
+        try:
+            a["workspace_bytes"] = ea.attn_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                                                                 a["d"])
+        except ea.AttnError:
+            a["workspace_bytes"] = 1 << 40  # invalid shape: the shape check must reject it by itself
+    return ea.attn_check_decode_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                     a["Nq"], a["Nk"], a["d"], a["scale"], a["workspace"], a["workspace_bytes"])
+
+
+def _plan(B, Hq, Hkv, Nq, Nk, d):
+    """The split plan the header documents: 128 packed rows per workgroup,
+    about 1024 workgroups, no empty key chunk."""
+    rows = (Hq // Hkv) * Nq
+    row_blocks = -(-rows // 128)
+    bn = 32 if d == 256 else 64
+    kv_tiles = -(-Nk // bn)
+    groups = B * Hkv * row_blocks
+    s = max(1, min(kv_tiles, -(-1024 // groups)))
+    chunk = -(-kv_tiles // s)
+    splits = -(-kv_tiles // chunk)
+    return groups, splits, groups * splits * 128 * (d + 1) * 4
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 1, 1, 1, 64), (1, 32, 8, 1, 8192, 256), (1, 32, 1, 1, 131072, 128), (4, 32, 8, 16, 4096, 128),
+    (2, 8, 2, 4, 1000, 64), (1, 64, 1, 16, 300, 128), (64, 32, 32, 1, 2048, 128),
+])
+def test_decode_workspace_size(shape):
+    groups, splits, nbytes = _plan(*shape)
+    assert ea.attn_decode_workspace_size(*shape) == nbytes
+    assert 1 <= splits and groups * splits < 2 * 1024 + groups
+
+
+def test_decode_workspace_size_empty_and_invalid():
+    assert ea.attn_decode_workspace_size(0, 8, 2, 4, 100, 128) == 0
+    assert ea.attn_decode_workspace_size(2, 8, 2, 0, 100, 128) == 0
+    with pytest.raises(ea.AttnError):
+        ea.attn_decode_workspace_size(2, 8, 2, 5, 4, 128)        # Nq > Nk
+    with pytest.raises(ea.AttnError):
+        ea.attn_decode_workspace_size(2, 8, 3, 1, 4, 128)        # Hq % Hkv != 0
+    with pytest.raises(ea.AttnError):
+        ea.attn_decode_workspace_size(2, 8, 2, 1, 4, 96)         # head_dim
+    lib = ea.load_library()
+    assert lib.attn_decode_workspace_size(1, 1, 1, 1, 1, 64, None) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_decode_valid_arguments():
+    assert dcheck() == ea.ATTN_OK
+    assert dcheck(lse=None) == ea.ATTN_OK
+    assert dcheck(Nq=1000) == ea.ATTN_OK                          # Nq == Nk
+    assert dcheck(Hkv=1) == ea.ATTN_OK and dcheck(Hkv=8) == ea.ATTN_OK
+    assert dcheck(scale=0.0) == ea.ATTN_OK and dcheck(scale=-1.0) == ea.ATTN_OK
+    for d in (64, 128, 256):
+        assert dcheck(d=d) == ea.ATTN_OK
+    assert dcheck(workspace_bytes=1 << 40) == ea.ATTN_OK          # larger than needed is fine
+    far = 1 << 44
+    assert dcheck(B=1, Hq=1, Hkv=1, Nq=1, Nk=(1 << 30) // 128, q=far, k=2 * far, v=3 * far, o=4 * far,
+                  lse=5 * far, workspace=6 * far) == ea.ATTN_OK
+
+
+def test_decode_empty_problems_are_ok_without_pointers():
+    none = dict(q=None, k=None, v=None, o=None, lse=None, workspace=None, workspace_bytes=0)
+    assert dcheck(B=0, **none) == ea.ATTN_OK
+    assert dcheck(Nq=0, **none) == ea.ATTN_OK
+
+
+@pytest.mark.parametrize("over", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(workspace=None),
+    dict(B=-1), dict(Nq=-1), dict(Nk=-1), dict(Hq=0), dict(Hkv=0), dict(Hq=8, Hkv=3),
+    dict(Nq=1001), dict(Nq=5, Nk=4),                               # more queries than positions
+    dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(Nk=(1 << 30) // 128 + 1, Nq=1),                           # Nk * d > 2^30
+    dict(workspace_bytes=0), dict(workspace_bytes=-5),
+    dict(o=P + 64),                                                # o overlaps q
+    dict(workspace=2 * P + 4096),                                  # workspace overlaps k
+    dict(workspace=4 * P - 64),                                    # workspace overlaps o
+    dict(lse=6 * P + 8),                                           # lse overlaps workspace
+    dict(lse=4 * P),                                               # lse overlaps o
+    dict(q=P + 2), dict(k=2 * P + 8), dict(o=4 * P + 4), dict(lse=5 * P + 2), dict(workspace=6 * P + 4),
+])
+def test_decode_invalid_arguments(over):
+    assert dcheck(**over) == ea.ATTN_ERR_INVALID_ARG, over
+
+
+def test_decode_short_workspace_is_rejected():
+    need = ea.attn_decode_workspace_size(2, 8, 2, 4, 1000, 128)
+    assert dcheck(workspace_bytes=need) == ea.ATTN_OK
+    assert dcheck(workspace_bytes=need - 1) == ea.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [32, 80, 96, 192])
+def test_decode_unsupported_head_dims(d):
+    assert dcheck(d=d, workspace_bytes=1 << 30) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_attn_decode_rejects_before_touching_the_device():
+    lib = ea.load_library()
+    st = lib.attn_decode(None, None, None, None, None, 1, 1, 1, 1, 16, 64, 0.125, 1, None, 0, None)
+    assert st == ea.ATTN_ERR_INVALID_ARG
+    st = lib.attn_decode(P, 2 * P, 3 * P, 4 * P, None, 1, 1, 1, 1, 16, 80, 0.125, 1, 6 * P, 1 << 20, None)
+    assert st == ea.ATTN_ERR_UNSUPPORTED
+    st = lib.attn_decode(P, 2 * P, 3 * P, 4 * P, None, 1, 1, 1, 1, 16, 64, 0.125, 1, 6 * P, 16, None)
+    assert st == ea.ATTN_ERR_INVALID_ARG                           # workspace too small
+    st = lib.attn_decode(None, None, None, None, None, 1, 4, 2, 0, 16, 64, 0.125, 1, None, 0, None)
+    assert st == ea.ATTN_OK
+
+
+def test_decode_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 1, 64, dtype=torch.float16)
+    k = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="AMD GPU"):
+        ea.attn_decode(q, k, k)

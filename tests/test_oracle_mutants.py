@@ -63,6 +63,17 @@ MUTANTS = {
                              "js = [j for j in blk if (not causal) or j < i]"),
     "online_lse_no_max": ("L_out.append(m + log(l))", "L_out.append(log(l))"),
     "online_max_ignores_old": ("m_new = max([m] + s)", "m_new = max(s)"),
+    # attention_decode_ref
+    "decode_no_offset": ("    pos = (Nk - Nq) + np.arange(Nq)", "    pos = np.arange(Nq)"),
+    "decode_offset_off_by_one": ("    pos = (Nk - Nq) + np.arange(Nq)", "    pos = (Nk - Nq - 1) + np.arange(Nq)"),
+    "decode_mask_strict": ("S = np.where(keys[None, :] <= pos[:, None], S, -np.inf)",
+                           "S = np.where(keys[None, :] < pos[:, None], S, -np.inf)"),
+    "decode_first_positions": ("S = np.where(keys[None, :] <= pos[:, None], S, -np.inf)",
+                               "S = np.where(keys[None, :] <= pos[:, None] - (Nk - Nq), S, -np.inf)"),
+    "decode_unnormalised": ("            O[b, hq] = (E / l[:, None]) @ V", "            O[b, hq] = E @ V"),
+    "decode_lse_no_max": ("            LSE[b, hq] = m + np.log(l)", "            LSE[b, hq] = np.log(l)"),
+    "decode_wrong_head": ("V = v[b, kvh].astype(np.float64)\n            S = sigma * (q[b, hq]",
+                          "V = v[b, hq % Hkv].astype(np.float64)\n            S = sigma * (q[b, hq]"),
 }
 
 
