@@ -10,6 +10,14 @@ the configuration the headline TFLOP/s metric is quoted on.  Prints ONE JSON
 line with the throughput, the roofline of the kernel (timed with HIP events on
 the launch stream), the CPU oracle timed on a bounded sample of the same
 workload, and a parity check of the timed output against that sample.
+
+    python bench.py --decode 1 [--steps K] [--warmup W]
+
+times the decode (KV-cache) path instead: a step is one attn_decode call (the
+per-chunk kernel and the merge kernel) on a named decode workload; the line
+reports HBM GB/s against the 8 TB/s peak.  When one copy of the cache is
+smaller than 1 GiB, the steps cycle over enough copies to exceed the chip's
+256 MB last-level cache, so that every step reads HBM.
 """
 
 from __future__ import annotations
@@ -25,7 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s + % of MI355X fp16 MFMA peak (N=2048, d=128)"
+DECODE_METRIC = "attention decode HBM GB/s + % of MI355X HBM peak"
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published figure
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published figure
 KERNEL_SOURCES = ["exact_attention_121_amd/csrc/attn_fwd_kernel.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 
@@ -111,6 +121,138 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, budget_s: float):
     return base, parity
 
 
+def calibration_copy(mib: int, dev):
+    """A plain elementwise copy of known traffic (y = -x in fp16, three
+    launches), against which hardware byte counters are scaled."""
+    import torch
+
+    n = mib * (1 << 20) // 2
+    x = torch.ones(n, dtype=torch.float16, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    return {"kernel": "torch.neg fp16 (elementwise)", "bytes_read": 2 * n, "bytes_written": 2 * n,
+            "launches": 3}
+
+
+def cpu_baseline_decode(w, q, k, v, o_gpu, lse_gpu, budget_s: float):
+    """Time the fp64 decode oracle one batch entry at a time until ~budget_s
+    of CPU work is done; check the GPU output of those entries against it."""
+    import numpy as np
+
+    from oracle.attention import attention_decode_ref
+
+    done, elapsed = 0, 0.0
+    max_err = mean_acc = lse_err = 0.0
+    for b in range(w.B):
+        t0 = time.perf_counter()
+        O_ref, L_ref = attention_decode_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1], w.scale, causal=w.causal)
+        elapsed += time.perf_counter() - t0
+        err = np.abs(o_gpu[b].astype(np.float64) - O_ref[0])
+        max_err = max(max_err, float(err.max()))
+        mean_acc += float(err.mean())
+        lse_err = max(lse_err, float(np.abs(lse_gpu[b] - L_ref[0]).max()))
+        done += 1
+        if elapsed >= budget_s:
+            break
+    value = done * (w.hbm_bytes / w.B) / elapsed / 1e9
+    base = {
+        "value": value,
+        "unit": "GB/s",
+        "cores": cpu_threads(),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B} batch entries (all {w.Hq} query heads, all {w.Nk} keys each), "
+                  f"{elapsed:.1f} s of fp64 numpy two-pass attention; GB/s counts the same "
+                  "algorithmic bytes as the GPU figure",
+    }
+    parity = {"batch_entries_checked": done, "max_abs_err_O": max_err, "mean_abs_err_O": mean_acc / done,
+              "max_abs_err_LSE": lse_err,
+              "ok": bool(max_err <= 1e-2 and mean_acc / done <= 1e-3 and lse_err <= 1e-3)}
+    return base, parity
+
+
+def run_decode(args) -> int:
+    import torch
+
+    import exact_attention_121_amd as ea
+    from exact_attention_121_amd.inputs import DECODE_WORKLOADS, make_decode_inputs
+
+    w = DECODE_WORKLOADS[args.decode]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ea.load_library()
+    q_np, k_np, v_np = make_decode_inputs(w)
+    kv_bytes = 2 * k_np.nbytes
+    copies = max(1, -(-(1 << 30) // kv_bytes))
+    q = torch.from_numpy(q_np).to(dev)
+    k0, v0 = torch.from_numpy(k_np).to(dev), torch.from_numpy(v_np).to(dev)
+    kvs = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, ea.attn_decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        kc, vc = kvs[i % copies]
+        ea.attn_decode(q, kc, vc, scale=w.scale, causal=w.causal, out=o, lse=lse, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    avg_step_ms = ev0.elapsed_time(ev1) / args.steps
+    value = w.hbm_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = w.hbm_bytes / (avg_step_ms * 1e-3) / 1e9
+    result = {
+        "metric": DECODE_METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: seeded N(0,sigma^2) fp16 Q and K/V cache at the workload's shape (no model weights)",
+        "config": {"workload": f"{w.name}: {w.describe()}", "global_batch": w.B, "new_queries": w.Nq,
+                   "cached_keys": w.Nk, "heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "causal": w.causal, "cache_copies_cycled": copies, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_step": w.hbm_bytes,
+                     "scope": "whole step: per-chunk kernel plus merge kernel"},
+        "kernel_ms": {"mean": round(avg_step_ms, 5), "timing": "HIP events on the launch stream around "
+                      f"all {args.steps} timed steps (two kernels per step)"},
+        "kernel_code_sha256_16": kernel_source_hash(),
+    }
+    if args.calibrate_copy_mib > 0:
+        result["copy_calibration"] = calibration_copy(args.calibrate_copy_mib, dev)
+    if not args.no_cpu_baseline:
+        step(0)  # the output of the first cache copy, which the oracle sees
+        torch.cuda.synchronize()
+        base, parity = cpu_baseline_decode(w, q_np, k_np, v_np, o.cpu().numpy(), lse.cpu().numpy(),
+                                           args.cpu_budget)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +262,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", type=int, default=0,
+                    help="time the decode path on this named decode workload (1-4) instead")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (fp16 -> fp16, "
                          "y = -x) three times, so that hardware byte counters can be "
@@ -131,6 +275,8 @@ def main() -> int:
               "the path shards over heads with no communication, but no multi-GPU run "
               "is part of it", file=sys.stderr)
         return 2
+    if args.decode:
+        return run_decode(args)
 
     import numpy as np
     import torch
@@ -198,15 +344,7 @@ def main() -> int:
         "kernel_code_sha256_16": kernel_source_hash(),
     }
     if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib * (1 << 20) // 2
-        x = torch.ones(n, dtype=torch.float16, device=dev)
-        y = torch.empty_like(x)
-        for _ in range(3):
-            torch.neg(x, out=y)
-        torch.cuda.synchronize()
-        result["copy_calibration"] = {"kernel": "torch.neg fp16 (elementwise)", "bytes_read": 2 * n,
-                                      "bytes_written": 2 * n, "launches": 3}
-        del x, y
+        result["copy_calibration"] = calibration_copy(args.calibrate_copy_mib, dev)
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, q_np, k_np, v_np, o.cpu().numpy(), lse.cpu().numpy(),
                                     args.cpu_budget)

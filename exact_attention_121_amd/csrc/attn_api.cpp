@@ -14,6 +14,9 @@
 namespace {
 
 constexpr int64_t kLimit31 = int64_t{1} << 31;
+// A dispatch holds fewer than 2^32 work-items: with 256 threads per
+// workgroup, fewer than 2^24 workgroups.
+constexpr int64_t kLimitGroups = int64_t{1} << 24;
 constexpr int64_t kLimitHead = int64_t{1} << 30;  // elements per head
 constexpr int64_t kRowsPerBlock = 128;  // query rows per workgroup
 
@@ -51,7 +54,7 @@ extern "C" int attn_check_args(const void* q, const void* k, const void* v, cons
   if (N > kLimitHead / d) return ATTN_ERR_INVALID_ARG;
   const int64_t q_tiles = (N + kRowsPerBlock - 1) / kRowsPerBlock;
   if (Hq >= kLimit31 || B >= kLimit31 / Hq) return ATTN_ERR_INVALID_ARG;
-  if (B * Hq >= kLimit31 / q_tiles) return ATTN_ERR_INVALID_ARG;  // grid < 2^31
+  if (B * Hq >= kLimitGroups / q_tiles) return ATTN_ERR_INVALID_ARG;  // workgroups < 2^24
 
   // B * Hq < 2^31 and N * d <= 2^30, so these byte counts fit in int64.
   const int64_t q_bytes = B * Hq * N * d * 2;
@@ -100,9 +103,11 @@ int check_decode_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t N
   if (Nq > Nk) return ATTN_ERR_INVALID_ARG;  // the queries are the last Nq of Nk positions
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (Nk > kLimitHead / d) return ATTN_ERR_INVALID_ARG;
-  if (Hq >= kLimit31 || B >= kLimit31 / Hq || B * Hq >= kLimit31 / Nq) return ATTN_ERR_INVALID_ARG;
+  // The merge runs d / 32 workgroups per query row.
+  if (Hq >= kLimit31 || B >= kLimit31 / Hq || B * Hq >= kLimitGroups / (Nq * (d / 32)))
+    return ATTN_ERR_INVALID_ARG;
   const attn::DecodePlan plan = attn::decode_plan(B, Hq, Hkv, Nq, Nk, d);
-  if (B * Hkv * plan.row_blocks >= kLimit31 / plan.splits) return ATTN_ERR_INVALID_ARG;  // grid < 2^31
+  if (B * Hkv * plan.row_blocks >= kLimitGroups / plan.splits) return ATTN_ERR_INVALID_ARG;
   return ATTN_OK;
 }
 

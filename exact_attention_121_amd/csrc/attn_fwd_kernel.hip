@@ -633,6 +633,8 @@ struct DecParams {
   const _Float16* q;
   const _Float16* k;
   const _Float16* v;
+  _Float16* o;      // final output, written here when there is one split
+  float* lse;       // final LSE (may be null), likewise
   float* part_o;    // [groups][splits][kDecodeRows][d]
   float* part_lse;  // [groups][splits][kDecodeRows], log2 units
   int Hq, Hkv, group, Nq, Nk, rows, row_blocks, splits, chunk_tiles;
@@ -727,6 +729,24 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_decode_split
   // none).
   const float l_tot = xlane_sum(w.l_run[0]);
   if (!valid) return;
+  if (p.splits == 1) {
+    // One chunk holds every key (key 0 among them, so l_tot > 0): finish the
+    // rows here, as the forward epilogue does, and skip the merge.
+    const float inv1 = 1.0f / l_tot;
+    _Float16* __restrict__ out = p.o + (((size_t)b * p.Hq + hq) * Nq + iq) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        half4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(w.oacc[0][dt][4 * rq + i] * inv1);
+        *reinterpret_cast<half4*>(out + 32 * dt + 8 * rq + 4 * w.g) = h;
+      }
+    if (p.lse != nullptr && w.g == 0)
+      p.lse[((size_t)b * p.Hq + hq) * Nq + iq] = (w.m_run[0] + __builtin_log2f(l_tot)) * kLn2;
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const size_t slot = ((size_t)grp * p.splits + split) * C::BM + 32 * wv + (lane & 31);
   float* __restrict__ orow = p.part_o + slot * D;
@@ -752,12 +772,28 @@ struct MergeParams {
   int Hq, Hkv, group, Nq, row_blocks, splits;
 };
 
-// One wave per query row (b, hq, i): LSE = log2 sum_s 2^LSE_s, then
-// O = sum_s 2^(LSE_s - LSE) O_s in fp32, rounded once to fp16.
-template <int D>
-__global__ __launch_bounds__(64) void attn_decode_merge_kernel(MergeParams p) {
-  constexpr int kPer = D / 64;  // dims per lane
-  const int rowid = blockIdx.x;  // (b * Hq + hq) * Nq + i
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 8;  // splits per thread whose loads are in flight together
+// Output dims per merge workgroup: a whole row when there are few splits
+// (fewer, fuller workgroups), 32-dim slices of it when there are many.
+constexpr int kMergeSliceDims = 32;
+constexpr int kMergeFewSplits = 64;
+
+// One workgroup per (query row (b, hq, i), DS output dims).  Each thread
+// folds a subset of the splits into its own (m, l, acc) with the online
+// rule (m = max LSE_s, l = sum 2^(LSE_s - m), acc = sum 2^(LSE_s - m) O_s),
+// reading each split's LSE and O slice in the same pass; the threads then
+// combine theirs: LSE = m + log2 l, O = acc / l, rounded once to fp16.
+template <int D, int DS>
+__global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(MergeParams p) {
+  constexpr int CH = DS / 4;                 // float4 chunks of a slice
+  constexpr int PAR = kMergeThreads / CH;    // splits read at once
+  constexpr int SLICES = D / DS;
+  __shared__ float sm_m[PAR][CH], sm_l[PAR][CH];
+  __shared__ float4 sm_acc[PAR][CH];
+
+  const int rowid = blockIdx.x / SLICES;     // (b * Hq + hq) * Nq + i
+  const int slice = blockIdx.x - rowid * SLICES;
   const int i = rowid % p.Nq;
   const int bh = rowid / p.Nq;
   const int hq = bh % p.Hq, b = bh / p.Hq;
@@ -765,27 +801,69 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(MergeParams p) {
   const int r = gq * p.Nq + i;
   const int grp = (b * p.Hkv + kvh) * p.row_blocks + r / (int)kDecodeRows;
   const int rr = r % (int)kDecodeRows;
-  const int lane = threadIdx.x;
-  const size_t base = (size_t)grp * p.splits;
+  const int tid = threadIdx.x, chunk = tid % CH, sp = tid / CH;
+  const int S = p.splits;
+  const float* __restrict__ lse_s = p.part_lse + (size_t)grp * S * kDecodeRows + rr;  // split s at s * kDecodeRows
+  const float* __restrict__ o_s =
+      p.part_o + ((size_t)grp * S * kDecodeRows + rr) * D + slice * DS + 4 * chunk;  // at s * kDecodeRows * D
 
-  float mx = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.part_lse[(base + s) * kDecodeRows + rr]);
-  float sum = 0.f;
-  for (int s = 0; s < p.splits; ++s) sum += __builtin_amdgcn_exp2f(p.part_lse[(base + s) * kDecodeRows + rr] - mx);
-  const float L = mx + __builtin_log2f(sum);  // key 0 is visible to every row: finite
-  float acc[kPer];
+  float m = -INFINITY, l = 0.f;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sp; s0 < S; s0 += PAR * kMergeBatch) {
+    // Issue the loads of kMergeBatch splits before using any (a split past
+    // the end reads split 0 and is then ignored).
+    float ls[kMergeBatch];
+    float4 x[kMergeBatch];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float wgt = __builtin_amdgcn_exp2f(p.part_lse[(base + s) * kDecodeRows + rr] - L);
-    const float* src = p.part_o + ((base + s) * kDecodeRows + rr) * D;
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int sk = s0 + k * PAR < S ? s0 + k * PAR : 0;
+      ls[k] = lse_s[(size_t)sk * kDecodeRows];
+      x[k] = *reinterpret_cast<const float4*>(o_s + (size_t)sk * kDecodeRows * D);
+    }
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) acc[e] += wgt * src[lane + 64 * e];
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (s0 + k * PAR < S && ls[k] > -INFINITY) {  // a split the row saw no key of adds nothing
+        const float mn = fmaxf(m, ls[k]);
+        const float a = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
+        const float w = __builtin_amdgcn_exp2f(ls[k] - mn);
+        l = l * a + w;
+        acc.x = acc.x * a + w * x[k].x;
+        acc.y = acc.y * a + w * x[k].y;
+        acc.z = acc.z * a + w * x[k].z;
+        acc.w = acc.w * a + w * x[k].w;
+        m = mn;
+      }
+    }
   }
-  _Float16* dst = p.o + (size_t)rowid * D;
+  sm_m[sp][chunk] = m;
+  sm_l[sp][chunk] = l;
+  sm_acc[sp][chunk] = acc;
+  __syncthreads();
+  if (tid < CH) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) dst[lane + 64 * e] = static_cast<_Float16>(acc[e]);
-  if (p.lse != nullptr && lane == 0) p.lse[rowid] = L * kLn2;
+    for (int k = 0; k < PAR; ++k) M = fmaxf(M, sm_m[k][tid]);  // finite: split 0 holds key 0
+    float L = 0.f;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < PAR; ++k) {
+      const float a = __builtin_amdgcn_exp2f(sm_m[k][tid] - M);  // 0 for threads that saw no split
+      const float4 x = sm_acc[k][tid];
+      L += a * sm_l[k][tid];
+      o.x += a * x.x;
+      o.y += a * x.y;
+      o.z += a * x.z;
+      o.w += a * x.w;
+    }
+    const float inv = 1.0f / L;
+    half4 h;
+    h[0] = static_cast<_Float16>(o.x * inv);
+    h[1] = static_cast<_Float16>(o.y * inv);
+    h[2] = static_cast<_Float16>(o.z * inv);
+    h[3] = static_cast<_Float16>(o.w * inv);
+    *reinterpret_cast<half4*>(p.o + (size_t)rowid * D + slice * DS + 4 * tid) = h;
+    if (p.lse != nullptr && slice == 0 && tid == 0) p.lse[rowid] = (M + __builtin_log2f(L)) * kLn2;
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -794,9 +872,13 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecParams& dp, const Merge
   hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL>), dim3(groups * static_cast<unsigned>(a.plan.splits)),
                      dim3(kThreads), 0, s, dp);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_merge_kernel<D>), dim3(static_cast<unsigned>(a.B) * a.Hq * a.Nq), dim3(64), 0,
-                     s, mp);
+  if (e != hipSuccess || a.plan.splits == 1) return e;
+  const unsigned rows = static_cast<unsigned>(a.B) * a.Hq * a.Nq;
+  if (a.plan.splits <= kMergeFewSplits)
+    hipLaunchKernelGGL((attn_decode_merge_kernel<D, D>), dim3(rows), dim3(kMergeThreads), 0, s, mp);
+  else
+    hipLaunchKernelGGL((attn_decode_merge_kernel<D, kMergeSliceDims>), dim3(rows * (D / kMergeSliceDims)),
+                       dim3(kMergeThreads), 0, s, mp);
   return hipGetLastError();
 }
 
@@ -843,6 +925,8 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   dp.q = static_cast<const _Float16*>(a.q);
   dp.k = static_cast<const _Float16*>(a.k);
   dp.v = static_cast<const _Float16*>(a.v);
+  dp.o = static_cast<_Float16*>(a.o);
+  dp.lse = a.lse;
   const int64_t groups = static_cast<int64_t>(a.B) * a.Hkv * a.plan.row_blocks;
   dp.part_o = static_cast<float*>(a.workspace);
   dp.part_lse = dp.part_o + groups * a.plan.splits * kDecodeRows * a.d;

@@ -29,10 +29,14 @@ int launch_forward(const LaunchArgs& a, void* stream);
 // into rows r = g * Nq + i (row blocks of kDecodeRows); the keys are split
 // into `splits` chunks of `chunk_tiles` key tiles, each chunk handled by one
 // workgroup that writes a partial O and LSE to the workspace; a second
-// kernel merges the partials.  Shared by the validation (workspace size) and
+// kernel merges the partials.  With one split the workgroups write O and LSE
+// themselves and the merge is not launched.  Shared by the validation (workspace size) and
 // the launcher so both see the same plan.
-constexpr int64_t kDecodeRows = 128;          // packed rows per workgroup
-constexpr int64_t kDecodeTargetGroups = 1024;  // enough workgroups to fill the chip
+constexpr int64_t kDecodeRows = 128;  // packed rows per workgroup
+
+// Workgroups the chip holds at once (256 CUs; two per CU with head_dim 64 or
+// 128, one with 256): the split count aims at one full round of them.
+inline int64_t decode_target_groups(int64_t d) { return d == 256 ? 256 : 512; }
 
 struct DecodePlan {
   int64_t row_blocks, kv_tiles, splits, chunk_tiles;
@@ -48,7 +52,8 @@ inline DecodePlan decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, in
   const int64_t bn = decode_key_tile(d);
   p.kv_tiles = (Nk + bn - 1) / bn;
   const int64_t groups = B * Hkv * p.row_blocks;
-  int64_t s = (kDecodeTargetGroups + groups - 1) / groups;
+  const int64_t target = decode_target_groups(d);
+  int64_t s = (target + groups - 1) / groups;
   if (s > p.kv_tiles) s = p.kv_tiles;
   if (s < 1) s = 1;
   p.chunk_tiles = (p.kv_tiles + s - 1) / s;

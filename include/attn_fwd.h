@@ -85,7 +85,8 @@ enum attn_status {
  *   causal 0 or non-zero
  *   stream HIP stream to queue the kernel on (NULL = default stream)
  *
- * Limits: N * d <= 2^30 and B * Hq * ceil(N / 128) < 2^31.  The output o (and
+ * Limits: N * d <= 2^30 and B * Hq * ceil(N / 128) < 2^24 (one dispatch of
+ * 256-thread workgroups holds fewer than 2^32 work-items).  The output o (and
  * lse) must not overlap q, k, v or each other.  q, k, v and o must be 16-byte
  * aligned and lse 4-byte aligned (ATTN_ERR_INVALID_ARG otherwise).
  * Returns an attn_status value.
@@ -129,10 +130,11 @@ int attn_check_args(const void* q, const void* k, const void* v, const void* o,
  *          overlap any other buffer, and two calls in flight must not share
  *          it.  Pointer alignment as for attn_fwd.
  *
- * Two kernels are queued on `stream` (the per-chunk pass, then the merge);
- * the call never synchronises.  Limits: Nk * d <= 2^30 and
- * B * Hq * Nq < 2^31.  Returns an attn_status value; on any status other
- * than ATTN_OK nothing has been launched.
+ * One or two kernels are queued on `stream` (the per-chunk pass, then the
+ * merge when the keys were split into more than one chunk); the call never
+ * synchronises.  Limits: Nk * d <= 2^30 and B * Hq * Nq * d / 32 < 2^24.
+ * Returns an attn_status value; on any status other than ATTN_OK nothing
+ * has been launched.
  */
 int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                 int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,

@@ -71,6 +71,9 @@ def test_valid_arguments():
     far = 1 << 44
     assert check(B=1, Hq=1, Hkv=1, N=(1 << 30) // 128, q=far, k=2 * far, v=3 * far, o=4 * far,
                  lse=5 * far) == ea.ATTN_OK
+    # The largest grid: 2^24 - 1 workgroups of 256 threads.
+    assert check(B=(1 << 24) - 1, Hq=1, Hkv=1, N=128, d=64, q=far, k=2 * far, v=3 * far, o=4 * far,
+                 lse=5 * far) == ea.ATTN_OK
 
 
 def test_empty_problems_are_ok_without_pointers():
@@ -85,6 +88,7 @@ def test_empty_problems_are_ok_without_pointers():
     dict(scale=float("inf")), dict(scale=float("-inf")), dict(scale=float("nan")),
     dict(N=(1 << 30) // 128 + 1), dict(N=1 << 40),             # N * d > 2^30
     dict(B=1 << 20, Hq=1 << 12, Hkv=1, N=128),                  # grid >= 2^31
+    dict(B=1 << 12, Hq=1 << 12, Hkv=1, N=128),                  # 2^24 workgroups: 2^32 work-items
     dict(o=P + 64),                                             # o overlaps q
     dict(o=2 * P + 4096),                                       # o overlaps k
     dict(lse=4 * P + 2),                                        # lse overlaps o
@@ -142,14 +146,15 @@ def dcheck(**over):
 
 
 def _plan(B, Hq, Hkv, Nq, Nk, d):
-    """The split plan the header documents: 128 packed rows per workgroup,
-    about 1024 workgroups, no empty key chunk."""
+    """The split plan: 128 packed rows per workgroup, splits aimed at one
+    round of resident workgroups (512; 256 with head_dim 256), no empty key
+    chunk; the workspace holds a partial O row and LSE per row slot."""
     rows = (Hq // Hkv) * Nq
     row_blocks = -(-rows // 128)
     bn = 32 if d == 256 else 64
     kv_tiles = -(-Nk // bn)
     groups = B * Hkv * row_blocks
-    s = max(1, min(kv_tiles, -(-1024 // groups)))
+    s = max(1, min(kv_tiles, -(-(256 if d == 256 else 512) // groups)))
     chunk = -(-kv_tiles // s)
     splits = -(-kv_tiles // chunk)
     return groups, splits, groups * splits * 128 * (d + 1) * 4
@@ -162,7 +167,7 @@ def _plan(B, Hq, Hkv, Nq, Nk, d):
 def test_decode_workspace_size(shape):
     groups, splits, nbytes = _plan(*shape)
     assert ea.attn_decode_workspace_size(*shape) == nbytes
-    assert 1 <= splits and groups * splits < 2 * 1024 + groups
+    assert 1 <= splits and groups * splits < 2 * 512 + groups
 
 
 def test_decode_workspace_size_empty_and_invalid():
@@ -205,6 +210,7 @@ def test_decode_empty_problems_are_ok_without_pointers():
     dict(scale=float("nan")), dict(scale=float("inf")),
     dict(Nk=(1 << 30) // 128 + 1, Nq=1),                           # Nk * d > 2^30
     dict(workspace_bytes=0), dict(workspace_bytes=-5),
+    dict(B=1 << 12, Hq=1 << 9, Hkv=1 << 9, Nq=2, Nk=4),              # merge: 2^24 workgroups
     dict(o=P + 64),                                                # o overlaps q
     dict(workspace=2 * P + 4096),                                  # workspace overlaps k
     dict(workspace=4 * P - 64),                                    # workspace overlaps o

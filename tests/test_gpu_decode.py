@@ -51,7 +51,8 @@ def test_named_decode_workload(wid):
 
 
 # (B, Hq, Hkv, Nq, Nk): packed rows G * Nq = 1, 2, 3, 24, 64, 144 (two row
-# blocks, ragged), 512 (four), Nq == Nk, one key, keys ending inside a tile.
+# blocks, ragged), 512 (four), Nq == Nk, one key, keys ending inside a tile,
+# and enough row blocks that the keys are not split at all.
 EDGE = [
     (1, 1, 1, 1, 1),
     (2, 2, 1, 1, 7),
@@ -63,6 +64,7 @@ EDGE = [
     (1, 4, 4, 5, 5),
     (1, 2, 1, 1, 4097),
     (2, 8, 8, 2, 33),
+    (64, 8, 8, 1, 200),      # 512 row blocks: one split, no merge, several key tiles
 ]
 
 
