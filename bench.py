@@ -36,17 +36,19 @@ METRIC = "attention fwd TFLOP/s + % of MI355X fp16 MFMA peak (N=2048, d=128)"
 DECODE_METRIC = "attention decode HBM GB/s + % of MI355X HBM peak"
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published figure
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published figure
-KERNEL_SOURCES = ["exact_attention_121_amd/csrc/attn_fwd_kernel.hip"]
+FORWARD_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_fwd_kernel.hip"]
+DECODE_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_decode_kernel.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_traffic.json")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=FORWARD_SOURCES) -> str:
     """Hash of the kernel sources with comments and blank lines removed, so
     that only a change of the code itself invalidates the stored counters."""
     import re
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -56,18 +58,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none for this workload or the kernel changed since."""
+def measured_traffic(workload_name: str, path=TRAFFIC_FILE, sources=FORWARD_SOURCES,
+                     key="hbm_bytes_per_launch"):
+    """HBM bytes per launch (per step for decode) from the committed rocprofv3
+    counter summary, or None when there is none for this workload or the
+    kernel changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     entry = rec.get(workload_name)
-    if not entry or entry.get("kernel_code_sha256_16") != kernel_source_hash():
+    if not entry or entry.get("kernel_code_sha256_16") != kernel_source_hash(sources):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry.get(key)
 
 
 def cpu_threads() -> int:
@@ -233,12 +237,13 @@ def run_decode(args) -> int:
                    "cached_keys": w.Nk, "heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
                    "causal": w.causal, "cache_copies_cycled": copies, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(w.name, DECODE_TRAFFIC_FILE, DECODE_SOURCES, "hbm_bytes_per_step"),
                      "bytes_per_step": w.hbm_bytes,
                      "scope": "whole step: per-chunk kernel plus merge kernel"},
         "kernel_ms": {"mean": round(avg_step_ms, 5), "timing": "HIP events on the launch stream around "
-                      f"all {args.steps} timed steps (two kernels per step)"},
-        "kernel_code_sha256_16": kernel_source_hash(),
+                      f"all {args.steps} timed steps (one or two kernels per step)"},
+        "kernel_code_sha256_16": kernel_source_hash(DECODE_SOURCES),
     }
     if args.calibrate_copy_mib > 0:
         result["copy_calibration"] = calibration_copy(args.calibrate_copy_mib, dev)

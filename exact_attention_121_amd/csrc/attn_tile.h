@@ -1,0 +1,439 @@
+// Device building blocks shared by the fused attention kernels for gfx950
+// (the prefill/forward kernel and the decode kernels): fragment types, the
+// LDS tile layout and its loads, the score / mask / online-softmax / P.V
+// steps of one key tile, and the software-pipelined iteration over key
+// tiles.  Included by the kernel sources only; everything lives in an
+// unnamed namespace.
+//
+// Pages cited:
+//   [CANN-FA]  www.mooersco.com/news/1200175 - "FlashAttention operator of the
+//              CANN ops-transformer repository: attention acceleration on the
+//              Ascend NPU"
+//   [FA-Dict]  hwcomputing.csdn.net/6a0dbd08662f9a54cb75eb74.html
+//   [FA-Infer] gitcode.csdn.net/6a0c62d2662f9a54cb75b31f.html
+#ifndef ATTN_TILE_H_
+#define ATTN_TILE_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4v lds_short4;
+
+constexpr int kThreads = 256;  // 4 waves of 64 lanes
+constexpr int kWaves = kThreads / 64;
+constexpr float kLn2 = 0.69314718055994531f;
+// Buffer resource word 3 for raw (unformatted, stride 0) buffer access on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Query blocks of 32 rows per wave, per head_dim.  Two blocks per wave let
+// every K/V operand read from LDS feed two matrix instructions and halve the
+// K/V traffic per query row (the workgroup covers 256 rows); that needs more
+// than 256 registers per lane, so those kernels run one wave per SIMD.
+#ifndef ATTN_QB64
+#define ATTN_QB64 1
+#endif
+#ifndef ATTN_QB128
+#define ATTN_QB128 1
+#endif
+#ifndef ATTN_QB256
+#define ATTN_QB256 1
+#endif
+template <int D>
+constexpr int query_blocks() {
+  return D == 64 ? ATTN_QB64 : (D == 128 ? ATTN_QB128 : ATTN_QB256);
+}
+
+template <int D>
+struct Cfg {
+  static constexpr int QB = query_blocks<D>();     // 32-row query blocks per wave
+  static constexpr int WAVE_ROWS = 32 * QB;        // query rows per wave
+  static constexpr int BM = kWaves * WAVE_ROWS;    // query rows per workgroup
+  static constexpr int BN = (D == 256) ? 32 : 64;  // keys per K/V tile
+  static constexpr int NT = BN / 32;               // 32-key sub-tiles of S^T
+  static constexpr int DC = D / 16;                // 16-dim k-steps of Q.K
+  static constexpr int DT = D / 32;                // 32-dim row tiles of O^T
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * D * 2;    // one K (or V) tile
+  static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
+  // Workgroups per CU the register budget allows.
+  static constexpr int WG_PER_CU = (QB == 1 && D != 256) ? 2 : 1;
+  // Matrix operands read from LDS ahead of their MFMA (K reads; twice as
+  // many V transpose reads, two per MFMA); measured on gfx950.
+  static constexpr int K_AHEAD = D == 256 ? 6 : 4;
+  static_assert(BN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
+};
+
+
+// Byte offset of 16-byte chunk `c` of row `r` inside a swizzled tile: the
+// chunk index is XORed with a function of the row's low four bits, chosen
+// (by exhaustive search over XOR-linear maps) so that both operand reads are
+// free of bank conflicts whether the LDS serves 128 or 256 bytes per clock:
+//   * K reads (ds_read_b128): 8 or 16 consecutive rows at one chunk;
+//   * V transpose reads (ds_read_b64_tr_b16): 4 consecutive keys x 4 chunks.
+// Rows of 256+ bytes use a 4-bit map; 128-byte rows (d = 64), where row
+// parity already selects the bank half, use a 3-bit map.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr uint64_t kMap16 = 0x73d962c8fb51ea40ull;  // f(r) for r = 0..15, 4 bits each
+  constexpr uint64_t kMap8 = 0x4703652156127430ull;   // 3-bit variant for 128-byte rows
+  constexpr uint64_t map = Cfg<D>::CPR >= 16 ? kMap16 : kMap8;
+  const int f = static_cast<int>((map >> (4 * (r & 15))) & 15);
+  return (r * Cfg<D>::CPR + (c ^ f)) * 16;
+}
+
+// Byte offsets, relative to a tile's first row, of the 16-byte chunks that
+// thread `tid` copies into a swizzled tile (the chunk that belongs at
+// position p % CPR of row p / CPR of the tile).
+template <int D>
+struct LoadOffsets {
+  uint32_t src[Cfg<D>::LOADS];
+  __device__ __forceinline__ void init(int tid) {
+    using C = Cfg<D>;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int p = i * kThreads + tid;  // destination chunk; lanes of a wave are consecutive
+      const int row = p / C::CPR;
+      const int chunk = (swz<D>(row, p % C::CPR) >> 4) - row * C::CPR;
+      src[i] = static_cast<uint32_t>((row * D + chunk * 8) * 2);
+    }
+  }
+};
+
+// A tile base at or above 2^31 bytes lies outside every K/V head (a head is
+// at most 2^31 bytes), so each read of the tile fails the buffer range check:
+// no memory is touched and the stage receives zeros.  Used for tiles past
+// the end of the loop, so that the load instructions need no branch.
+constexpr uint32_t kSkipTile = 0x80000000u;
+
+// Queue the copy of the tile whose first row starts at byte `base` of one K
+// or V head into a swizzled LDS tile.  Rows at or past N read as zeros
+// (buffer range check).
+template <int D>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, char* tile, uint32_t base,
+                                          const LoadOffsets<D>& lo, int tid) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    char* dst = tile + (i * kThreads + (tid & ~63)) * 16;  // wave-uniform base
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, static_cast<int>(base + lo.src[i]),
+                                             0, 0, 0);
+  }
+}
+
+// Byte offset of the first row of key tile j inside a head, or kSkipTile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_base(int j, int nt) {
+  return j < nt ? static_cast<uint32_t>(j) * (Cfg<D>::BN * D * 2) : kSkipTile;
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ short4v tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+}
+
+__device__ __forceinline__ float xlane_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+__device__ __forceinline__ float xlane_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
+// Per-lane LDS byte offsets of the matrix operands inside a (swizzled) tile.
+// Tile rows 32*t + 16*h (K) or key groups (V) only add a constant, so every
+// operand read is one of these registers plus an immediate offset.
+template <int D>
+struct Offsets {
+  int k[Cfg<D>::DC];       // K rows lane%32 (+32 t), chunk 2 dc + lane/32
+  int v[2][Cfg<D>::DT];    // V keys 4 g + (lane%16)/4 (+8 for [1]), dims of row tile dt
+  __device__ __forceinline__ void init(int lane) {
+    using C = Cfg<D>;
+    const int lr = lane & 31, g = lane >> 5, m16 = lane & 15;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) k[dc] = swz<D>(lr, 2 * dc + g);
+    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);  // dim offset inside a 32-dim tile
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int dim = 32 * dt + dsub;
+        v[hi][dt] = swz<D>(4 * g + (m16 >> 2) + 8 * hi, dim >> 3) + (dim & 7) * 2;
+      }
+  }
+};
+
+template <int D>
+using STile = f32x16[Cfg<D>::QB][Cfg<D>::NT];  // logits of one key tile, per query block
+template <int D>
+using PTile = half8[Cfg<D>::QB][Cfg<D>::NT][2];  // fp16 probabilities of one key tile
+template <int D>
+using OAcc = f32x16[Cfg<D>::QB][Cfg<D>::DT];  // output accumulators O^T
+template <int D>
+using QFrag = half8[Cfg<D>::QB][Cfg<D>::DC];  // Q rows as B operands
+
+// S^T = K Q^T for one key tile: s[qb][t] holds keys 32 t .. 32 t + 31 (rows
+// of the 32x32 result) against query block qb (columns).  Each K operand
+// read from LDS serves every query block of the wave.
+template <int D>
+__device__ __forceinline__ void qk_tile(const char* ks, const QFrag<D>& qf, const Offsets<D>& off,
+                                        STile<D>& s) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) s[qb][t] = f32x16{};
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      const half8 a = *reinterpret_cast<const half8*>(ks + off.k[dc] + 32 * t * C::CPR * 16);
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+        s[qb][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[qb][dc], s[qb][t], 0, 0, 0);
+    }
+}
+
+// Keys past the end of the sequence, or after the query when causal, get
+// logit -inf (then exp2 gives exactly 0).  Lane L holds keys
+// 32 t + 8 (r/4) + 4 (L/32) + r%4 of query row `qrow` (+32 per block).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void mask_tile(STile<D>& s, int kv0, int N, int qrow, int g) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = key < N && (!CAUSAL || key <= qrow + 32 * qb);
+        s[qb][t][r] = ok ? s[qb][t][r] : -INFINITY;
+      }
+}
+
+// Row maxima of a tile's raw logits, in log2 units (c > 0).
+template <int D>
+__device__ __forceinline__ void tile_max(const STile<D>& s, float c, float (&m)[Cfg<D>::QB]) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    float mx = s[qb][0][0];
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int r = (t == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[qb][t][r]);
+    m[qb] = xlane_max(mx) * c;
+  }
+}
+
+// The running maximum m is only raised when some row of the wave saw a logit
+// more than kLazy (log2 units) above it.  Probabilities are taken relative
+// to m, so they stay <= 2^kLazy (exact in fp16, no overflow in fp32) and the
+// result is the same function: every term of the numerator and of l shares
+// the same reference m, which cancels in O = sum(p v) / sum(p) and is added
+// back in LSE = m + log2 l.
+constexpr float kLazy = 8.0f;
+
+template <int D>
+__device__ __forceinline__ void raise_max(const float (&m_tile)[Cfg<D>::QB], float (&m_run)[Cfg<D>::QB],
+                                          float (&l_run)[Cfg<D>::QB], OAcc<D>& oacc) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    if (__any(m_tile[qb] > m_run[qb] + kLazy)) {
+      const float m_new = fmaxf(m_run[qb], m_tile[qb]);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // 0 while m_run = -inf
+      m_run[qb] = m_new;
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) oacc[qb][dt] *= alpha;
+    }
+  }
+}
+
+// P = exp2(c S - m) rounded to fp16: the B operand of the P.V product, in
+// the lane's own key order.
+template <int D>
+__device__ __forceinline__ void softmax_tile(const STile<D>& s, float c, const float (&m_run)[Cfg<D>::QB],
+                                             PTile<D>& pf) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pf[qb][t][r >> 3][r & 7] =
+            static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][t][r], c, -m_run[qb])));
+}
+
+// Adds the sum of the fp16 probabilities (exactly the values multiplied
+// into V) to the lane's partial row sums l.
+template <int D>
+__device__ __forceinline__ void add_row_sums(const PTile<D>& pf, float (&l_run)[Cfg<D>::QB]) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+      {
+        const half8 x = pf[qb][t][h];
+        l0 = __builtin_amdgcn_fdot2(half2v{x[0], x[1]}, half2v{1.0f16, 1.0f16}, l0, false);
+        l1 = __builtin_amdgcn_fdot2(half2v{x[2], x[3]}, half2v{1.0f16, 1.0f16}, l1, false);
+        l0 = __builtin_amdgcn_fdot2(half2v{x[4], x[5]}, half2v{1.0f16, 1.0f16}, l0, false);
+        l1 = __builtin_amdgcn_fdot2(half2v{x[6], x[7]}, half2v{1.0f16, 1.0f16}, l1, false);
+      }
+    l_run[qb] += l0 + l1;
+  }
+}
+
+// O^T += V^T P^T for one key tile.  The A operand pairs B slot j of lane
+// group g with key 8 (j/4) + 4 g + j%4 (+16 h, +32 t): two transpose reads of
+// four keys each from V in its natural [key][dim] layout, shared by every
+// query block of the wave.
+template <int D>
+__device__ __forceinline__ void pv_tile(const char* vs, const PTile<D>& pf, const Offsets<D>& off,
+                                        OAcc<D>& oacc) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kb = (32 * t + 16 * h) * C::CPR * 16;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const short4v lo = tr_read(vs + off.v[0][dt] + kb);
+        const short4v hi = tr_read(vs + off.v[1][dt] + kb);
+        const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb)
+          oacc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[qb][t][h], oacc[qb][dt], 0, 0, 0);
+      }
+    }
+}
+
+// Per-wave state of the software pipeline.
+template <int D>
+struct WaveState {
+  QFrag<D> qf;
+  OAcc<D> oacc;
+  Offsets<D> off;
+  float m_run[Cfg<D>::QB], l_run[Cfg<D>::QB];
+  float c;
+  int N, qw0, qrow, g, nt_w;  // qrow: row of this lane in block 0; nt_w: key tiles this wave computes
+};
+
+// LDS layout: K tiles in stages 0/1, then V tiles in stages 0/1.
+template <int D>
+__device__ __forceinline__ char* k_stage(char* smem, int st) { return smem + st * Cfg<D>::TILE_BYTES; }
+template <int D>
+__device__ __forceinline__ char* v_stage(char* smem, int st) { return smem + (2 + st) * Cfg<D>::TILE_BYTES; }
+
+// Instruction groups for the compiler's scheduler (masks of
+// __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100;
+
+// Iteration j of the pipeline ([CANN-FA] section "Concrete flow": scores,
+// online-softmax update and P.V for key block j).  On entry K_{j+1} sits in
+// K stage (j+1)&1, V_j in V stage j&1, and s_cur holds the masked logits of
+// tile j with the running max already raised for them.  The matrix cores
+// compute S_{j+1} = K_{j+1} Q^T while the vector ALUs turn s_cur into P_j;
+// then O += P_j V_j runs while the vector ALUs reduce S_{j+1}.  Meanwhile
+// V_{j+1} and K_{j+2} stream into the stages freed by the previous iteration
+// ([CANN-FA] section "Ascend C implementation": load the next block while the
+// current one is computed).
+template <int D, bool CAUSAL, int PAR>
+__device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
+                                              __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                              const LoadOffsets<D>& lo, int tid, WaveState<D>& w,
+                                              STile<D>& s_cur, STile<D>& s_nxt) {
+  using C = Cfg<D>;
+  const uint32_t v_base = tile_base<D>(j + 1, nt);
+  const uint32_t k_base = tile_base<D>(j + 2, nt);
+  if (j < w.nt_w) {
+    load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), v_base, lo, tid);
+    load_tile<D>(krs, k_stage<D>(smem, PAR), k_base, lo, tid);
+    // S_{j+1} is computed even past this wave's last tile (reading a stale
+    // but in-bounds stage) so that the matrix and vector work stay in one
+    // block the scheduler can interleave; it is discarded then.
+    qk_tile<D>(k_stage<D>(smem, PAR ^ 1), w.qf, w.off, s_nxt);
+    PTile<D> pf;
+    softmax_tile<D>(s_cur, w.c, w.m_run, pf);
+    // Materialise P_j here, so that the compiler keeps the softmax next to
+    // the S_{j+1} product instead of sinking it past the mask branch.
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(pf[qb][t][h]));
+    if constexpr (C::DC >= 8) {
+      // One MFMA of S_{j+1}, then a share of the softmax of tile j; a K
+      // operand read per group of query blocks; the V/K copies ride along.
+      // (With d = 64 the compiler's own order measured faster.)
+      constexpr int kMfma = C::DC * C::NT * C::QB;
+      constexpr int kValu = (3 * 16 * C::NT * C::QB + kMfma - 1) / kMfma;
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, C::K_AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, kValu, 0);
+        if (i % C::QB == C::QB - 1) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        if (i < 2 * C::LOADS) __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+      }
+    }
+    const int kv1 = (j + 1) * C::BN;
+    if (kv1 + C::BN > w.N || (CAUSAL && kv1 + C::BN - 1 > w.qw0))
+      mask_tile<D, CAUSAL>(s_nxt, kv1, w.N, w.qrow, w.g);
+    // Raised issue priority while this wave feeds the matrix cores with
+    // P_j V_j, so that the other wave of the SIMD fills the gaps with its
+    // vector work rather than the reverse.
+    __builtin_amdgcn_s_setprio(1);
+    pv_tile<D>(v_stage<D>(smem, PAR), pf, w.off, w.oacc);
+    add_row_sums<D>(pf, w.l_run);
+    float m_tile[C::QB];
+    tile_max<D>(s_nxt, w.c, m_tile);
+    if constexpr (C::DC >= 8) {
+      // One MFMA of P_j V_j, then V operand reads and a share of the
+      // row-max reduction of S_{j+1}.
+      constexpr int kMfma = C::NT * 2 * C::DT * C::QB;
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2 * C::K_AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        if (i % C::QB == C::QB - 1) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 2, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (j + 1 < w.nt_w) raise_max<D>(m_tile, w.m_run, w.l_run, w.oacc);
+  } else {
+    load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), v_base, lo, tid);
+    load_tile<D>(krs, k_stage<D>(smem, PAR), k_base, lo, tid);
+  }
+  wait_vm_all();
+  __syncthreads();
+}
+
+}  // namespace
+}  // namespace attn
+
+#endif  // ATTN_TILE_H_
