@@ -11,6 +11,8 @@ attention  plain two-pass fp64 attention (numpy), the reference every GPU
            result is compared with (also for decode steps, where the queries
            are the last positions of the cached sequence), plus the online-softmax recurrence in the
            pages' own step order (used only to pin the two-pass form).
+backward   the gradients (dQ, dK, dV) of that forward, from the chain rule,
+           for the GPU backward pass.
 brute      the textbook softmax definition written as scalar loops over
            mpmath numbers, with no max-subtraction, for tiny inputs.
 
@@ -22,9 +24,11 @@ Pages cited (the text of three web pages on one subject):
   [FA-Infer] gitcode.csdn.net page 6a0c62d2662f9a54cb75b31f (why Transformer
              inference is slow; FlashAttention on Ascend and CANN)
 
-Parity status: every function here is pinned by tests/test_oracle_pins.py
-against closed forms, invariants, brute force and mutation tests; none is
-"parity unpinned".
+Parity status: every function here is pinned -- the forward and decode
+functions by tests/test_oracle_pins.py (closed forms, invariants, brute
+force, mutation tests), the backward by tests/test_oracle_bwd.py (finite
+differences of the forward, torch autograd, invariants, mutation tests);
+none is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -34,3 +38,4 @@ from .attention import (  # noqa: F401
     online_attention,
     kv_head_of,
 )
+from .backward import attention_bwd_delta, attention_bwd_ref  # noqa: F401
