@@ -11,6 +11,12 @@ line with the throughput, the roofline of the kernel (timed with HIP events on
 the launch stream), the CPU oracle timed on a bounded sample of the same
 workload, and a parity check of the timed output against that sample.
 
+    python bench.py --backward [--workload 2]
+
+times the backward pass instead: a step is one attn_bwd call (three kernels)
+given the forward's O and LSE; FLOPs are 10 d per visible (query, key) pair
+(the four gradient products and the recomputed scores).
+
     python bench.py --decode 1 [--steps K] [--warmup W]
 
 times the decode (KV-cache) path instead: a step is one attn_decode call (the
@@ -34,12 +40,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s + % of MI355X fp16 MFMA peak (N=2048, d=128)"
 DECODE_METRIC = "attention decode HBM GB/s + % of MI355X HBM peak"
+BACKWARD_METRIC = "attention bwd TFLOP/s + % of MI355X fp16 MFMA peak"
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published figure
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published figure
 FORWARD_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_fwd_kernel.hip"]
 DECODE_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_decode_kernel.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_traffic.json")
+BACKWARD_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_bwd_kernel.hip"]
+BACKWARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_traffic.json")
 
 
 def kernel_source_hash(sources=FORWARD_SOURCES) -> str:
@@ -258,6 +267,127 @@ def run_decode(args) -> int:
     return 0
 
 
+def cpu_baseline_backward(w, q, k, v, do, grads, budget_s: float):
+    """Time the fp64 backward oracle on whole (batch, query head) pairs (for
+    GQA, the group's key/value head gets that query head's share) until about
+    budget_s of CPU work is done; check dQ of those heads against it and dK,
+    dV where the group has one query head."""
+    import numpy as np
+
+    from oracle.backward import attention_bwd_ref
+
+    G = w.Hq // w.Hkv
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    done, elapsed = 0, 0.0
+    worst = {"dQ": 0.0, "dK": 0.0, "dV": 0.0}
+    ok = True
+    for b, h in heads:
+        g = h // G
+        sl_q = (slice(b, b + 1), slice(h, h + 1))
+        sl_k = (slice(b, b + 1), slice(g, g + 1))
+        t0 = time.perf_counter()
+        ref = attention_bwd_ref(q[sl_q], k[sl_k], v[sl_k], do[sl_q], w.scale, causal=w.causal)
+        elapsed += time.perf_counter() - t0
+        checks = [("dQ", grads[0][sl_q], ref[0])]
+        if G == 1:
+            checks += [("dK", grads[1][sl_k], ref[1]), ("dV", grads[2][sl_k], ref[2])]
+        for name, x, r in checks:
+            err = np.abs(x.astype(np.float64) - r)
+            worst[name] = max(worst[name], float(err.max() / np.abs(r).max()))
+            ok &= bool(err.max() <= 1e-2 * np.abs(r).max() and err.mean() <= 2e-3 * np.abs(r).mean())
+        done += 1
+        if elapsed >= budget_s:
+            break
+    per_head = 10 * w.d * (w.pairs // w.B // w.Hq)
+    base = {
+        "value": done * per_head / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cpu_threads(),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (batch, head) pairs, all {w.N} rows each, {elapsed:.1f} s of fp64 "
+                  "numpy chain-rule backward",
+    }
+    parity = {"heads_checked": done, "max_rel_err": worst, "ok": ok}
+    return base, parity
+
+
+def run_backward(args) -> int:
+    import numpy as np
+    import torch
+
+    import exact_attention_121_amd as ea
+    from exact_attention_121_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ea.load_library()
+    q_np, k_np, v_np = make_inputs(w)
+    do_np = np.random.default_rng(w.seed + 7).standard_normal(q_np.shape, dtype=np.float32).astype(np.float16)
+    q, k, v, do = (torch.from_numpy(x).to(dev) for x in (q_np, k_np, v_np, do_np))
+    o, lse = ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, ea.attn_bwd_workspace_size(w.B, w.Hq, w.N, w.d)), dtype=torch.uint8, device=dev)
+
+    def step():
+        ea.attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    avg_step_ms = ev0.elapsed_time(ev1) / args.steps
+    flops = 10 * w.d * w.pairs
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_step_ms * 1e-3) / 1e12
+    result = {
+        "metric": BACKWARD_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: seeded N(0,1) fp16 Q/K/V and upstream gradient dO at the workload's shape",
+        "config": {"workload": f"{w.name} backward: {w.describe()}", "global_batch": w.B, "seq_len": w.N,
+                   "heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "causal": w.causal,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, BACKWARD_TRAFFIC_FILE, BACKWARD_SOURCES,
+                                                 "hbm_bytes_per_step"),
+                     "flops_per_step": flops,
+                     "scope": "whole step: prep, dK/dV and dQ kernels; 10 d FLOPs per visible pair"},
+        "kernel_ms": {"mean": round(avg_step_ms, 5), "timing": "HIP events on the launch stream around "
+                      f"all {args.steps} timed steps (three kernels per step)"},
+        "kernel_code_sha256_16": kernel_source_hash(BACKWARD_SOURCES),
+    }
+    if args.calibrate_copy_mib > 0:
+        result["copy_calibration"] = calibration_copy(args.calibrate_copy_mib, dev)
+    if not args.no_cpu_baseline:
+        grads = [x.cpu().numpy() for x in (dq, dk, dv)]
+        base, parity = cpu_baseline_backward(w, q_np, k_np, v_np, do_np, grads, args.cpu_budget)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +399,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", type=int, default=0,
                     help="time the decode path on this named decode workload (1-4) instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dQ, dK, dV) on --workload instead")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (fp16 -> fp16, "
                          "y = -x) three times, so that hardware byte counters can be "
@@ -282,6 +414,8 @@ def main() -> int:
         return 2
     if args.decode:
         return run_decode(args)
+    if args.backward:
+        return run_backward(args)
 
     import numpy as np
     import torch

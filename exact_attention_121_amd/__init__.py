@@ -1,7 +1,9 @@
-"""Fused exact-attention forward for AMD Instinct MI355X (gfx950).
+"""Fused exact attention for AMD Instinct MI355X (gfx950).
 
-    from exact_attention_121_amd import attn_fwd
+    from exact_attention_121_amd import attn_fwd, attn_bwd, attn_decode
     o, lse = attn_fwd(q, k, v, causal=True)     # torch fp16 tensors on the GPU
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=True)
+    o1, lse1 = attn_decode(q_new, k_cache, v_cache)
 
 The computation runs in hand-written HIP kernels behind a C ABI
 (include/attn_fwd.h, libattn_fwd.so); this package is the thin binding,
@@ -17,7 +19,10 @@ from .binding import (  # noqa: F401
     AttnArgumentError,
     AttnError,
     AttnUnsupportedError,
+    attn_bwd,
+    attn_bwd_workspace_size,
     attn_check_args,
+    attn_check_bwd_args,
     attn_check_decode_args,
     attn_decode,
     attn_decode_workspace_size,
@@ -27,4 +32,4 @@ from .binding import (  # noqa: F401
     load_library,
 )
 
-__version__ = "0.2.0"
+__version__ = "0.3.0"

@@ -22,7 +22,8 @@ ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_DEVICE = 3
 
 EXPORTS = ("attn_fwd", "attn_check_args", "attn_decode", "attn_decode_workspace_size",
-           "attn_check_decode_args", "attn_status_string", "attn_version")
+           "attn_check_decode_args", "attn_bwd", "attn_bwd_workspace_size", "attn_check_bwd_args",
+           "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -68,6 +69,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_check_decode_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                            ctypes.c_float, vp, i64]
     lib.attn_check_decode_args.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                             ctypes.c_int, vp, i64, vp]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64)]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_int
+    lib.attn_check_bwd_args.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                        ctypes.c_float, vp, i64]
+    lib.attn_check_bwd_args.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -225,3 +234,81 @@ def attn_decode(q, k, v, *, scale: float | None = None, causal: bool = True, out
             workspace.data_ptr() or None, ws_bytes, s.cuda_stream or None)
     _raise_for(status)
     return out, lse
+
+
+def attn_bwd_workspace_size(B, Hq, N, d) -> int:
+    """Workspace bytes attn_bwd needs for this shape (host only)."""
+    out = ctypes.c_int64(0)
+    _raise_for(load_library().attn_bwd_workspace_size(B, Hq, N, d, ctypes.byref(out)))
+    return out.value
+
+
+def attn_check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace,
+                        workspace_bytes) -> int:
+    """Host-only validation of attn_bwd (pointers as integers or None); returns a status."""
+    return load_library().attn_check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d,
+                                              float(scale), workspace, workspace_bytes)
+
+
+def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool = False, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """Attention backward on torch tensors resident on one AMD GPU.
+
+    q, o, dout: [B, Hq, N, d] fp16 and k, v: [B, Hkv, N, d] fp16, with o and
+    lse ([B, Hq, N] fp32) as attn_fwd returned them for the same q, k, v,
+    scale and causal.  Returns (dq, dk, dv) shaped like q, k, v.
+    ``workspace`` is an optional uint8 device tensor of at least
+    attn_bwd_workspace_size(...) bytes (allocated here when omitted).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be torch.float16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on an AMD GPU (torch 'cuda' device), got {t.device}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on q's device")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must be shaped like q")
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, Hq, N) or lse.dtype != torch.float32
+            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be the contiguous fp32 [B, Hq, N] tensor attn_fwd returned")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            t = torch.empty_like(like)
+        elif (t.shape != like.shape or t.dtype != torch.float16 or t.device != q.device
+              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp16 tensor shaped like its input")
+        outs.append(t)
+    dq, dk, dv = outs
+    need = attn_bwd_workspace_size(B, Hq, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = lib.attn_bwd(
+            q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+            lse.data_ptr() or None, dout.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
+            dv.data_ptr() or None, B, Hq, Hkv, N, d, float(scale), 1 if causal else 0,
+            workspace.data_ptr() or None, ws_bytes, s.cuda_stream or None)
+    _raise_for(status)
+    return dq, dk, dv

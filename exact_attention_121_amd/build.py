@@ -22,7 +22,7 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattn_fwd.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attn_fwd_kernel.hip", "attn_decode_kernel.hip"]
+HIP_SOURCES = ["attn_fwd_kernel.hip", "attn_decode_kernel.hip", "attn_bwd_kernel.hip"]
 CXX_SOURCES = ["attn_api.cpp"]
 DEPS = ["attn_launch.h", "attn_tile.h", os.path.join("..", "..", "include", "attn_fwd.h")]
 

@@ -176,6 +176,88 @@ extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o,
   return attn::launch_decode(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
+extern "C" int attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t N, int64_t d, int64_t* bytes) {
+  if (bytes == nullptr || B < 0 || N < 0 || Hq < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) {
+    *bytes = 0;
+    return ATTN_OK;
+  }
+  if (N > kLimitHead / d || Hq >= kLimit31 || B >= kLimit31 / Hq) return ATTN_ERR_INVALID_ARG;
+  *bytes = attn::bwd_workspace_bytes(B, Hq, N);
+  return ATTN_OK;
+}
+
+extern "C" int attn_check_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                   const void* dout, const void* dq, const void* dk, const void* dv, int64_t B,
+                                   int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
+                                   const void* workspace, int64_t workspace_bytes) {
+  if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) return ATTN_OK;  // empty problem: nothing to touch
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
+    return ATTN_ERR_INVALID_ARG;
+  if (misaligned_tensors(q, k, v, o, lse) || misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) ||
+      misaligned(dv, 16) || misaligned(workspace, 16))
+    return ATTN_ERR_INVALID_ARG;
+  if (N > kLimitHead / d) return ATTN_ERR_INVALID_ARG;
+  if (Hq >= kLimit31 || B >= kLimit31 / Hq) return ATTN_ERR_INVALID_ARG;
+  const int64_t q_tiles = (N + kRowsPerBlock - 1) / kRowsPerBlock;
+  // Workgroups of the dQ and dK/dV kernels, and of the per-row preparation
+  // (d / 8 lanes per row), each below 2^24; padded rows fit in int.
+  if (B * Hq >= kLimitGroups / q_tiles) return ATTN_ERR_INVALID_ARG;
+  const int64_t rows = B * Hq * attn::bwd_padded_rows(N);
+  if (rows >= kLimit31 || rows / (256 / (d / 8)) >= kLimitGroups) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn::bwd_workspace_bytes(B, Hq, N)) return ATTN_ERR_INVALID_ARG;
+  const int64_t q_bytes = B * Hq * N * d * 2;
+  const int64_t kv_bytes = B * Hkv * N * d * 2;
+  const int64_t lse_bytes = B * Hq * N * 4;
+  const int64_t ws_bytes = attn::bwd_workspace_bytes(B, Hq, N);
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  const int64_t in_bytes[6] = {q_bytes, kv_bytes, kv_bytes, q_bytes, lse_bytes, q_bytes};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const int64_t out_bytes[4] = {q_bytes, kv_bytes, kv_bytes, ws_bytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ATTN_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                        int64_t N, int64_t d, float scale, int causal, void* workspace, int64_t workspace_bytes,
+                        struct ihipStream_t* stream) {
+  const int st = attn_check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace,
+                                     workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (B == 0 || N == 0) return ATTN_OK;
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.workspace = workspace;
+  a.B = static_cast<int>(B);
+  a.Hq = static_cast<int>(Hq);
+  a.Hkv = static_cast<int>(Hkv);
+  a.N = static_cast<int>(N);
+  a.d = static_cast<int>(d);
+  a.scale = scale;
+  a.causal = causal != 0;
+  return attn::launch_backward(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
 extern "C" const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK:
@@ -191,4 +273,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" const char* attn_version(void) { return "attn_fwd 0.2.0 gfx950"; }
+extern "C" const char* attn_version(void) { return "attn_fwd 0.3.0 gfx950"; }

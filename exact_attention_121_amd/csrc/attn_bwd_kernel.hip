@@ -1,0 +1,461 @@
+// Fused attention backward for gfx950: dQ, dK, dV from Q, K, V, the
+// forward's O and LSE, and the upstream gradient dO.
+//
+// The pages name training as a use of the operator ([CANN-FA], opening
+// paragraph) and note that backpropagation must keep gradients ([FA-Dict]
+// section "Standard attention"); the gradients follow from the forward
+// definition ([CANN-FA] section "Where is the bottleneck of standard
+// attention") by the chain rule:
+//   P  = exp(scale Q K^T - LSE)          (recomputed tile by tile from the
+//                                         stored LSE: no N x N matrix)
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - Delta),  Delta_i = dO_i . O_i
+//   dQ = scale dS K,  dK = scale dS^T Q
+// As in the forward, S and P never leave the chip.
+//
+// Three kernels:
+//   * attn_bwd_prep_kernel: Delta_i and LSE_i * log2(e) per query row, into a
+//     workspace padded to whole 128-row tiles (padding rows: Delta = 0 and
+//     LSE = +inf, so that their probabilities are exactly 0 with no bounds
+//     check).
+//   * attn_bwd_dkdv_kernel: one workgroup per 128 keys of one key/value head
+//     (32 per wave, the lanes' columns; with head_dim 256, per half of the
+//     output dims as well); K and V stay in registers as matrix
+//     operands; the Q and dO tiles of every query head of the group stream
+//     through LDS.  Per query tile: S = Q K^T and dP = dO V^T on the matrix
+//     cores, P and dS on the vector ALUs, then dV^T += dO^T P and
+//     dK^T += Q^T dS with P and dS used straight from registers and the
+//     transposed tiles read with ds_read_b64_tr_b16 (the forward's P.V step).
+//   * attn_bwd_dq_kernel: one workgroup per 128 query rows, shaped like the
+//     forward kernel: S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T.
+// The two main kernels recompute S and dP each; there are no atomics, and
+// every output element is written once.
+//
+// Pages cited:
+//   [CANN-FA]  www.mooersco.com/news/1200175
+//   [FA-Dict]  hwcomputing.csdn.net/6a0dbd08662f9a54cb75eb74.html
+
+#include "attn_tile.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdParams {
+  const _Float16* q;
+  const _Float16* k;
+  const _Float16* v;
+  const _Float16* o;
+  const _Float16* dout;
+  const float* lse;   // forward LSE, natural log, [B][Hq][N]
+  _Float16* dq;
+  _Float16* dk;
+  _Float16* dv;
+  float* lse2;        // workspace [B][Hq][Npad]: LSE * log2(e); +inf past N
+  float* delta;       // workspace [B][Hq][Npad]: dO . O; 0 past N
+  int N, Npad, Hq, Hkv, group, rows_total;
+  float c;            // scale * log2(e), any sign
+  float scale;
+};
+
+// ---------------------------------------------------------------------------
+// Delta and LSE in log2 units.  D / 8 lanes per row (16-byte loads), the
+// row's partial dot products summed with lane shuffles.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(BwdParams p) {
+  constexpr int CH = D / 8;                 // lanes per row
+  constexpr int ROWS = kThreads / CH;       // rows per workgroup
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x * ROWS + tid / CH;   // (b * Hq + hq) * Npad + i
+  const int part = tid % CH;
+  if (row >= p.rows_total) return;          // whole lane groups leave together
+  const int bh = row / p.Npad;
+  const int i = row - bh * p.Npad;
+  float acc = 0.f;
+  if (i < p.N) {
+    const size_t off = ((size_t)bh * p.N + i) * D + part * 8;
+    const half8 a = *reinterpret_cast<const half8*>(p.o + off);
+    const half8 g = *reinterpret_cast<const half8*>(p.dout + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += static_cast<float>(a[e]) * static_cast<float>(g[e]);
+  }
+#pragma unroll
+  for (int w = CH / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
+  if (part == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = i < p.N ? p.lse[(size_t)bh * p.N + i] * kLog2e : INFINITY;
+  }
+}
+
+// Probabilities and dS of one tile from the scores s and dP, with per-entry
+// LSE (log2) and Delta: P = exp2(c s - lse2), masked entries (arg = -inf)
+// give exactly 0; dS = P (dP - delta).  Both rounded to fp16 as the B
+// operands of the following products (the forward's P layout).
+template <int D>
+__device__ __forceinline__ void p_and_ds(const STile<D>& arg, const STile<D>& dp, const float (&delta)[Cfg<D>::NT][16],
+                                         PTile<D>& pf, PTile<D>& dsf) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(arg[0][t][r]);
+      pf[0][t][r >> 3][r & 7] = static_cast<_Float16>(pv);
+      dsf[0][t][r >> 3][r & 7] = static_cast<_Float16>(pv * (dp[0][t][r] - delta[t][r]));
+    }
+}
+
+// Output dim tiles per dK/dV workgroup: with head_dim 256 the two halves of
+// the dims go to two workgroups (each recomputes S and dP), so that the dK
+// and dV accumulators fit in the register file next to K and V.
+template <int D>
+constexpr int bwd_dim_parts() { return D == 256 ? 2 : 1; }
+
+// pv_tile over NDT of the 32-dim output tiles, whose transpose-read lane
+// offsets are in voff (the dims of those tiles only).
+template <int D, int NDT>
+__device__ __forceinline__ void pv_tile_part(const char* vs, const PTile<D>& pf, const int (&voff)[2][NDT],
+                                             f32x16 (&acc)[NDT]) {
+  using C = Cfg<D>;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kb = (32 * t + 16 * h) * C::CPR * 16;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const short4v lo = tr_read(vs + voff[0][i] + kb);
+        const short4v hi = tr_read(vs + voff[1][i] + kb);
+        const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[0][t][h], acc[i], 0, 0, 0);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  Query tiles of BN rows stream through LDS (Q in the "K" stages,
+// dO in the "V" stages); the wave's 32 keys are the columns of S and dP.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p, int k_tiles) {
+  using C = Cfg<D>;
+  static_assert(C::QB == 1, "one 32-key block per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
+
+  constexpr int NP = bwd_dim_parts<D>();
+  constexpr int NDT = C::DT / NP;       // 32-dim output tiles of this workgroup
+  const int part = blockIdx.x % NP;
+  const int kt = (blockIdx.x / NP) % k_tiles;
+  const int bk = blockIdx.x / NP / k_tiles;   // b * Hkv + kvh
+  const int b = bk / p.Hkv, kvh = bk - b * p.Hkv;
+  const int N = p.N;
+  const int k0 = kt * kBwdKeys;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int kw0 = k0 + 32 * wv;          // first key of this wave
+  const int key = kw0 + (lane & 31);     // this lane's key (column)
+
+  // K and V rows of the wave as B operands (dims 16 dc + 8 g .. +7).
+  const size_t kvoff = (size_t)bk * N * D;
+  QFrag<D> kf, vf;
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) {
+    const size_t e = kvoff + (size_t)key * D + 16 * dc + 8 * g;
+    kf[0][dc] = key < N ? *reinterpret_cast<const half8*>(p.k + e) : half8{};
+    vf[0][dc] = key < N ? *reinterpret_cast<const half8*>(p.v + e) : half8{};
+  }
+  f32x16 dk_acc[NDT], dv_acc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) {
+    dk_acc[i] = f32x16{};
+    dv_acc[i] = f32x16{};
+  }
+  Offsets<D> off;
+  off.init(lane);
+  // Transpose-read offsets of this workgroup's output dims (as Offsets::init).
+  int voff[2][NDT];
+  {
+    const int m16 = lane & 15;
+    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const int dim = 32 * (part * NDT + i) + dsub;
+        voff[hi][i] = swz<D>(4 * g + (m16 >> 2) + 8 * hi, dim >> 3) + (dim & 7) * 2;
+      }
+  }
+  LoadOffsets<D> lo;
+  lo.init(tid);
+
+  // Steps: (query head of the group, query tile), query tiles from the one
+  // holding key k0 (causal) to the end.
+  const int q_tiles = (N + C::BN - 1) / C::BN;
+  const int qt0 = CAUSAL ? k0 / C::BN : 0;
+  const int nq = q_tiles - qt0;
+  const int steps = p.group * nq;
+  const int head_bytes = static_cast<int>(static_cast<uint32_t>(N) * (D * 2));
+  auto issue = [&](int u, int st) {
+    const int gq = u < steps ? u / nq : 0;
+    const int qt = u < steps ? qt0 + (u - gq * nq) : 0;
+    const size_t qoff = ((size_t)b * p.Hq + kvh * p.group + gq) * N * D;
+    const __amdgpu_buffer_rsrc_t qrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qoff), (short)0, head_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t drs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + qoff), (short)0, head_bytes, kBufferWord3);
+    const uint32_t base = tile_base<D>(u < steps ? qt : 0, u < steps ? q_tiles : 0);
+    load_tile<D>(qrs, k_stage<D>(smem, st), base, lo, tid);
+    load_tile<D>(drs, v_stage<D>(smem, st), base, lo, tid);
+  };
+
+  issue(0, 0);
+  wait_vm_all();
+  __syncthreads();
+  for (int u = 0; u < steps; ++u) {
+    const int st = u & 1;
+    const int gq = u / nq;
+    const int q0 = (qt0 + (u - gq * nq)) * C::BN;
+    // Causal: skip tiles whose every query precedes every key of the wave
+    // (wave-uniform, as the matrix instructions need).
+    const bool active = kw0 < N && !(CAUSAL && q0 + C::BN - 1 < kw0);
+    // Per-entry LSE and Delta (entry r of sub-tile t is query
+    // q0 + 32 t + 8 (r / 4) + 4 g + r % 4), loaded before the next tile's
+    // copies are queued so that waiting for them does not wait for those.
+    float lse2[C::NT][16], delta[C::NT][16];
+    if (active) {
+      const size_t rowbase = ((size_t)b * p.Hq + kvh * p.group + gq) * p.Npad + q0;
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const size_t e = rowbase + 32 * t + 8 * rr + 4 * g;
+          const float4 l4 = *reinterpret_cast<const float4*>(p.lse2 + e);
+          const float4 d4 = *reinterpret_cast<const float4*>(p.delta + e);
+          lse2[t][4 * rr + 0] = l4.x;
+          lse2[t][4 * rr + 1] = l4.y;
+          lse2[t][4 * rr + 2] = l4.z;
+          lse2[t][4 * rr + 3] = l4.w;
+          delta[t][4 * rr + 0] = d4.x;
+          delta[t][4 * rr + 1] = d4.y;
+          delta[t][4 * rr + 2] = d4.z;
+          delta[t][4 * rr + 3] = d4.w;
+        }
+    }
+    issue(u + 1, st ^ 1);
+    if (active) {
+      STile<D> s, dp;
+      qk_tile<D>(k_stage<D>(smem, st), kf, off, s);    // S = Q K^T: rows queries, columns keys
+      qk_tile<D>(v_stage<D>(smem, st), vf, off, dp);   // dP = dO V^T
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[0][t][r] = __builtin_fmaf(s[0][t][r], p.c, -lse2[t][r]);
+      if (CAUSAL && q0 < kw0 + 31) {
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qrow = q0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+            s[0][t][r] = key <= qrow ? s[0][t][r] : -INFINITY;
+          }
+      }
+      PTile<D> pf, dsf;
+      p_and_ds<D>(s, dp, delta, pf, dsf);
+      pv_tile_part<D, NDT>(v_stage<D>(smem, st), pf, voff, dv_acc);    // dV^T += dO^T P
+      pv_tile_part<D, NDT>(k_stage<D>(smem, st), dsf, voff, dk_acc);   // dK^T += Q^T dS
+    }
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  if (key >= N) return;
+  _Float16* __restrict__ dkrow = p.dk + kvoff + (size_t)key * D;
+  _Float16* __restrict__ dvrow = p.dv + kvoff + (size_t)key * D;
+#pragma unroll
+  for (int i = 0; i < NDT; ++i)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      half4 hk, hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hk[e] = static_cast<_Float16>(dk_acc[i][4 * rq + e] * p.scale);
+        hv[e] = static_cast<_Float16>(dv_acc[i][4 * rq + e]);
+      }
+      const int dim0 = 32 * (part * NDT + i) + 8 * rq + 4 * g;
+      *reinterpret_cast<half4*>(dkrow + dim0) = hk;
+      *reinterpret_cast<half4*>(dvrow + dim0) = hv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Like the forward kernel: 128 query rows per workgroup (32 per wave,
+// the lanes' columns), K and V tiles stream through LDS.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(BwdParams p, int q_tiles) {
+  using C = Cfg<D>;
+  static_assert(C::QB == 1, "one 32-row block per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
+
+  int qt = blockIdx.x % q_tiles;
+  const int bh = blockIdx.x / q_tiles;   // b * Hq + hq
+  if (CAUSAL) qt = q_tiles - 1 - qt;     // heaviest tiles first
+  const int b = bh / p.Hq, hq = bh - b * p.Hq, kvh = hq / p.group;
+  const int N = p.N;
+  const int q0 = qt * C::BM;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int qw0 = q0 + 32 * wv;
+  const int row = qw0 + (lane & 31);
+
+  const size_t qoff = (size_t)bh * N * D;
+  QFrag<D> qf, df;
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) {
+    const size_t e = qoff + (size_t)row * D + 16 * dc + 8 * g;
+    qf[0][dc] = row < N ? *reinterpret_cast<const half8*>(p.q + e) : half8{};
+    df[0][dc] = row < N ? *reinterpret_cast<const half8*>(p.dout + e) : half8{};
+  }
+  const float lse2 = p.lse2[(size_t)bh * p.Npad + row];   // +inf past N
+  const float delta = p.delta[(size_t)bh * p.Npad + row];
+  OAcc<D> dq_acc;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) dq_acc[0][dt] = f32x16{};
+  Offsets<D> off;
+  off.init(lane);
+  LoadOffsets<D> lo;
+  lo.init(tid);
+
+  const size_t kvoff = ((size_t)b * p.Hkv + kvh) * N * D;
+  const int head_bytes = static_cast<int>(static_cast<uint32_t>(N) * (D * 2));
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvoff), (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvoff), (short)0, head_bytes, kBufferWord3);
+
+  const int kv_tiles = (N + C::BN - 1) / C::BN;
+  int nt = kv_tiles;
+  if (CAUSAL) {
+    const int last_q = (q0 + C::BM < N ? q0 + C::BM : N) - 1;
+    nt = last_q / C::BN + 1 < kv_tiles ? last_q / C::BN + 1 : kv_tiles;
+  }
+  int nt_w = nt;  // key tiles this wave needs
+  if (qw0 >= N) {
+    nt_w = 0;
+  } else if (CAUSAL) {
+    const int last_w = (qw0 + 32 < N ? qw0 + 32 : N) - 1;
+    nt_w = last_w / C::BN + 1;
+  }
+
+  load_tile<D>(krs, k_stage<D>(smem, 0), 0, lo, tid);
+  load_tile<D>(vrs, v_stage<D>(smem, 0), 0, lo, tid);
+  wait_vm_all();
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    const int st = j & 1;
+    const uint32_t nb = tile_base<D>(j + 1, nt);
+    load_tile<D>(krs, k_stage<D>(smem, st ^ 1), nb, lo, tid);
+    load_tile<D>(vrs, v_stage<D>(smem, st ^ 1), nb, lo, tid);
+    if (j < nt_w) {
+      STile<D> s, dp;
+      qk_tile<D>(k_stage<D>(smem, st), qf, off, s);    // S^T = K Q^T
+      qk_tile<D>(v_stage<D>(smem, st), df, off, dp);   // dP^T = V dO^T
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[0][t][r] = __builtin_fmaf(s[0][t][r], p.c, -lse2);
+      const int kv0 = j * C::BN;
+      if (kv0 + C::BN > N || (CAUSAL && kv0 + C::BN - 1 > qw0)) mask_tile<D, CAUSAL>(s, kv0, N, row, g);
+      float dl[C::NT][16];
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dl[t][r] = delta;
+      PTile<D> pf, dsf;
+      p_and_ds<D>(s, dp, dl, pf, dsf);
+      pv_tile<D>(k_stage<D>(smem, st), dsf, off, dq_acc);   // dQ^T += K^T dS^T
+    }
+    wait_vm_all();
+    __syncthreads();
+  }
+
+  if (row >= N) return;
+  _Float16* __restrict__ out = p.dq + qoff + (size_t)row * D;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      half4 h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(dq_acc[0][dt][4 * rq + i] * p.scale);
+      *reinterpret_cast<half4*>(out + 32 * dt + 8 * rq + 4 * g) = h;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
+  using C = Cfg<D>;
+  constexpr int rows_per_wg = kThreads / (D / 8);
+  const unsigned prep_grid = static_cast<unsigned>((p.rows_total + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3(prep_grid), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int k_tiles = (a.N + kBwdKeys - 1) / kBwdKeys;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>),
+                     dim3(static_cast<unsigned>(a.B) * a.Hkv * k_tiles * bwd_dim_parts<D>()), dim3(kThreads), 0, s,
+                     p, k_tiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int q_tiles = (a.N + C::BM - 1) / C::BM;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(static_cast<unsigned>(a.B) * a.Hq * q_tiles),
+                     dim3(kThreads), 0, s, p, q_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_backward(const BwdArgs& a, void* stream) {
+  BwdParams p;
+  p.q = static_cast<const _Float16*>(a.q);
+  p.k = static_cast<const _Float16*>(a.k);
+  p.v = static_cast<const _Float16*>(a.v);
+  p.o = static_cast<const _Float16*>(a.o);
+  p.dout = static_cast<const _Float16*>(a.dout);
+  p.lse = a.lse;
+  p.dq = static_cast<_Float16*>(a.dq);
+  p.dk = static_cast<_Float16*>(a.dk);
+  p.dv = static_cast<_Float16*>(a.dv);
+  p.N = a.N;
+  p.Npad = static_cast<int>(bwd_padded_rows(a.N));
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.group = a.Hq / a.Hkv;
+  p.rows_total = a.B * a.Hq * p.Npad;
+  p.lse2 = static_cast<float*>(a.workspace);
+  p.delta = p.lse2 + static_cast<size_t>(p.rows_total);
+  p.c = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
+  p.scale = a.scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (a.d) {
+    case 64:
+      e = a.causal ? launch_bwd_t<64, true>(a, p, s) : launch_bwd_t<64, false>(a, p, s);
+      break;
+    case 128:
+      e = a.causal ? launch_bwd_t<128, true>(a, p, s) : launch_bwd_t<128, false>(a, p, s);
+      break;
+    case 256:
+      e = a.causal ? launch_bwd_t<256, true>(a, p, s) : launch_bwd_t<256, false>(a, p, s);
+      break;
+    default:
+      e = hipErrorInvalidValue;
+  }
+  return static_cast<int>(e);
+}
+
+}  // namespace attn

@@ -78,6 +78,34 @@ struct DecodeArgs {
 // Queues the split kernel and the merge kernel on `stream`.
 int launch_decode(const DecodeArgs& a, void* stream);
 
+// Backward: keys per dK/dV workgroup (32 per wave) and the workspace rows
+// per (batch, query head): N rounded up to whole 128-row query tiles.
+constexpr int64_t kBwdKeys = 128;
+inline int64_t bwd_padded_rows(int64_t N) { return (N + 127) / 128 * 128; }
+// Workspace: LSE in log2 units and Delta = dO . O, fp32, per padded row.
+inline int64_t bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t N) {
+  return 2 * B * Hq * bwd_padded_rows(N) * 4;
+}
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;
+  int B, Hq, Hkv, N, d;
+  float scale;
+  int causal;
+};
+
+// Queues the three backward kernels (prep, dK/dV, dQ) on `stream`.
+int launch_backward(const BwdArgs& a, void* stream);
+
 }  // namespace attn
 
 #endif  // ATTN_LAUNCH_H_

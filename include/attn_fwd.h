@@ -160,10 +160,66 @@ int attn_check_decode_args(const void* q, const void* k, const void* v,
                            int64_t d, float scale, const void* workspace,
                            int64_t workspace_bytes);
 
+/*
+ * attn_bwd - fused attention backward: the gradients of attn_fwd's O with
+ * respect to q, k and v, given the upstream gradient dout of O.
+ *
+ * The pages name training as a use of the operator ([CANN-FA], opening
+ * paragraph) and backpropagation's need to keep gradients ([FA-Dict] section
+ * "Standard attention"); the gradients are the chain rule applied to
+ * attn_fwd's definition: with P = exp(scale q k^T - lse) (masked entries 0),
+ * dv = P^T dout, dP = dout v^T, dS = P o (dP - rowsum(dout o o)),
+ * dq = scale dS k, dk = scale dS^T q (summed over the query heads that share
+ * a key/value head).  P is recomputed from q, k and lse; nothing N x N is
+ * stored.
+ *
+ *   q, o, dout   [B][Hq][N][d]  fp16, read only (o as attn_fwd wrote it)
+ *   k, v         [B][Hkv][N][d] fp16, read only
+ *   lse          [B][Hq][N]     fp32, read only: attn_fwd's lse (required)
+ *   dq           [B][Hq][N][d]  fp16, written: every element once
+ *   dk, dv       [B][Hkv][N][d] fp16, written: every element once
+ *   B, Hq, Hkv, N, d, scale, causal, stream: as for attn_fwd (the same
+ *          values the forward ran with)
+ *   workspace, workspace_bytes: caller-owned device memory of at least
+ *          attn_bwd_workspace_size(...) bytes (per-row fp32 terms); contents
+ *          on entry do not matter, on return unspecified; must not overlap
+ *          any other buffer; two calls in flight must not share it.
+ *
+ * Three kernels are queued on `stream`; the call never synchronises.  The
+ * outputs must not overlap the inputs, each other or the workspace.  Every
+ * pointer is 16-byte aligned (lse 4-byte).  Limits as for attn_fwd, and
+ * B * Hq * round_up(N, 128) < 2^31.  Returns an attn_status value; on any
+ * status other than ATTN_OK nothing has been launched.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+             float scale, int causal, void* workspace, int64_t workspace_bytes,
+             struct ihipStream_t* stream);
+
+/*
+ * attn_bwd_workspace_size - bytes of workspace attn_bwd needs (0 for an
+ * empty problem), written to *bytes.  Host only.  ATTN_ERR_INVALID_ARG for
+ * a NULL bytes or invalid sizes, ATTN_ERR_UNSUPPORTED for other head_dims.
+ */
+int attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t N, int64_t d,
+                            int64_t* bytes);
+
+/*
+ * attn_check_bwd_args - the argument validation of attn_bwd on the host
+ * only (pointers compared, never dereferenced; no HIP call).
+ */
+int attn_check_bwd_args(const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        const void* dq, const void* dk, const void* dv,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                        int64_t d, float scale, const void* workspace,
+                        int64_t workspace_bytes);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Static version string of the library, e.g. "attn_fwd 0.2.0 gfx950". */
+/* Static version string of the library, e.g. "attn_fwd 0.3.0 gfx950". */
 const char* attn_version(void);
 
 #ifdef __cplusplus

@@ -251,3 +251,100 @@ def test_decode_binding_refuses_cpu_tensors():
     k = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError, match="AMD GPU"):
         ea.attn_decode(q, k, k)
+
+
+# --- backward entry points ---------------------------------------------------
+
+BGOOD = dict(q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, dout=6 * P, dq=7 * P, dk=8 * P, dv=9 * P,
+             B=2, Hq=8, Hkv=2, N=1000, d=128, scale=0.125, workspace=10 * P, workspace_bytes=None)
+
+
+def bcheck(**over):
+    a = dict(BGOOD, **over)
+    if a["workspace_bytes"] is None:
+        try:
+            a["workspace_bytes"] = ea.attn_bwd_workspace_size(a["B"], a["Hq"], a["N"], a["d"])
+        except ea.AttnError:
+            a["workspace_bytes"] = 1 << 40
+    return ea.attn_check_bwd_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                                  a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"], a["workspace"],
+                                  a["workspace_bytes"])
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 64), (2, 8, 1000, 128), (1, 32, 8192, 256), (3, 5, 129, 64)])
+def test_bwd_workspace_size(shape):
+    B, Hq, N, d = shape
+    npad = -(-N // 128) * 128
+    assert ea.attn_bwd_workspace_size(*shape) == 2 * B * Hq * npad * 4
+
+
+def test_bwd_workspace_size_empty_and_invalid():
+    assert ea.attn_bwd_workspace_size(0, 8, 100, 128) == 0
+    assert ea.attn_bwd_workspace_size(2, 8, 0, 128) == 0
+    with pytest.raises(ea.AttnError):
+        ea.attn_bwd_workspace_size(2, 8, 100, 96)
+    with pytest.raises(ea.AttnError):
+        ea.attn_bwd_workspace_size(-1, 8, 100, 128)
+    assert ea.load_library().attn_bwd_workspace_size(1, 1, 1, 64, None) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_bwd_valid_arguments():
+    assert bcheck() == ea.ATTN_OK
+    assert bcheck(scale=0.0) == ea.ATTN_OK and bcheck(scale=-0.3) == ea.ATTN_OK
+    for d in (64, 128, 256):
+        assert bcheck(d=d) == ea.ATTN_OK
+    assert bcheck(Hkv=8) == ea.ATTN_OK and bcheck(Hkv=1) == ea.ATTN_OK
+    assert bcheck(workspace_bytes=1 << 40) == ea.ATTN_OK
+
+
+def test_bwd_empty_problems_are_ok_without_pointers():
+    none = dict(q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None, dv=None, workspace=None,
+                workspace_bytes=0)
+    assert bcheck(B=0, **none) == ea.ATTN_OK
+    assert bcheck(N=0, **none) == ea.ATTN_OK
+
+
+@pytest.mark.parametrize("over", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(dout=None),
+    dict(dq=None), dict(dk=None), dict(dv=None), dict(workspace=None),
+    dict(B=-1), dict(N=-1), dict(Hq=0), dict(Hkv=0), dict(Hq=8, Hkv=3), dict(scale=float("nan")),
+    dict(N=(1 << 30) // 128 + 1),
+    dict(workspace_bytes=0),
+    dict(dq=P + 16),                        # dq overlaps q
+    dict(dk=5 * P),                         # dk overlaps lse
+    dict(dv=7 * P + 64),                    # dv overlaps dq
+    dict(workspace=9 * P + 4096),           # workspace overlaps dv
+    dict(dq=6 * P + 4096),                  # dq overlaps dout
+    dict(q=P + 2), dict(dout=6 * P + 8), dict(dk=8 * P + 4), dict(lse=5 * P + 2), dict(workspace=10 * P + 4),
+])
+def test_bwd_invalid_arguments(over):
+    assert bcheck(**over) == ea.ATTN_ERR_INVALID_ARG, over
+
+
+@pytest.mark.parametrize("d", [32, 80, 96, 192])
+def test_bwd_unsupported_head_dims(d):
+    assert bcheck(d=d, workspace_bytes=1 << 30) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_bwd_short_workspace_is_rejected():
+    need = ea.attn_bwd_workspace_size(2, 8, 1000, 128)
+    assert bcheck(workspace_bytes=need) == ea.ATTN_OK
+    assert bcheck(workspace_bytes=need - 1) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_attn_bwd_rejects_before_touching_the_device():
+    lib = ea.load_library()
+    nulls = [None] * 9
+    assert lib.attn_bwd(*nulls, 1, 1, 1, 16, 64, 0.125, 1, None, 0, None) == ea.ATTN_ERR_INVALID_ARG
+    ptrs = [P * (i + 1) for i in range(9)]
+    assert lib.attn_bwd(*ptrs, 1, 1, 1, 16, 80, 0.125, 1, 10 * P, 1 << 20, None) == ea.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_bwd(*ptrs, 1, 1, 1, 16, 64, 0.125, 1, 10 * P, 8, None) == ea.ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd(*nulls, 0, 4, 2, 16, 64, 0.125, 1, None, 0, None) == ea.ATTN_OK
+
+
+def test_bwd_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError, match="AMD GPU"):
+        ea.attn_bwd(x, x, x, x, lse, x)

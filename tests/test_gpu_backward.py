@@ -1,0 +1,139 @@
+"""GPU parity of the backward pass (dQ, dK, dV) against the fp64 CPU oracle.
+
+The GPU runs its own forward (attn_fwd) for O and LSE, then attn_bwd; the
+oracle computes the exact gradients of the same definition from Q, K, V, dO.
+
+Bar, per gradient X in {dQ, dK, dV} (no NaN/Inf anywhere):
+    max |X_gpu - X_ref| <= 1e-2 * max |X_ref|
+    mean |X_gpu - X_ref| <= 2e-3 * mean |X_ref|
+The GPU rounds P and dS to fp16 before the products that use them (relative
+error <= 2^-11 each), takes Delta from the fp16 O, and rounds the gradients
+to fp16 (2^-11 relative); everything else accumulates in fp32.  The bound on
+the worst element is five times the fp16 half-ulp, relative to the largest
+gradient; the mean is held to about the half-ulp.  Where the exact gradient
+is identically zero (a single key), |X_gpu| <= 1e-5.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from exact_attention_121_amd.inputs import WORKLOADS, make_inputs, make_qkv
+from oracle.backward import attention_bwd_ref
+from parity_util import to_dev
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 1e-2
+MEAN_REL = 2e-3
+ZERO_ABS = 1e-5
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_dout(shape, seed):
+    """Upstream gradient: N(0, 1) fp16, its own seed (drawn like Q)."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+
+
+def gpu_backward(q, k, v, do, scale, causal):
+    import torch
+
+    import exact_attention_121_amd as ea
+    tq, tk, tv, tdo = to_dev(q, k, v, do)
+    o, lse = ea.attn_fwd(tq, tk, tv, scale=scale, causal=causal)
+    dq, dk, dv = ea.attn_bwd(tq, tk, tv, o, lse, tdo, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def assert_grad_parity(got, ref, what):
+    stats = []
+    for name, x, r in zip(("dQ", "dK", "dV"), got, ref):
+        x = np.asarray(x, dtype=np.float64)
+        assert x.shape == r.shape, f"{what} {name}: shape {x.shape} vs {r.shape}"
+        assert np.isfinite(x).all(), f"{what} {name}: non-finite values"
+        err = np.abs(x - r)
+        ref_max = float(np.abs(r).max()) if r.size else 0.0
+        ref_mean = float(np.abs(r).mean()) if r.size else 0.0
+        mx, mean = float(err.max(initial=0.0)), float(err.mean() if err.size else 0.0)
+        stats.append(f"{name} max {mx:.2e} (ref {ref_max:.2e}) mean {mean:.2e} (ref {ref_mean:.2e})")
+        if ref_max == 0.0:
+            # The exact gradient vanishes (one key: P = 1, dS = 0).  The GPU's
+            # dS is P (dP - Delta) with Delta from the fp16 O, so it is
+            # rounding noise: far below the fp16 resolution of unit values.
+            assert mx <= ZERO_ABS, f"{what} {name}: expected zeros, max |err| {mx:.3e}"
+            continue
+        assert mx <= MAX_REL * ref_max, f"{what} {name}: max |err| {mx:.3e} > {MAX_REL} * {ref_max:.3e}"
+        assert mean <= MEAN_REL * ref_mean, f"{what} {name}: mean |err| {mean:.3e} > {MEAN_REL} * {ref_mean:.3e}"
+    _say(f"[bwd] {what}: " + "; ".join(stats))
+
+
+# (B, Hq, Hkv, N): one key, ragged tails around the 32/64/128 tile sizes,
+# GQA and MQA groupings.
+EDGE = [(1, 1, 1, 1), (1, 2, 1, 7), (2, 4, 2, 63), (1, 4, 4, 65), (1, 2, 1, 129), (2, 8, 2, 300),
+        (1, 4, 1, 777), (1, 2, 2, 1000)]
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", EDGE)
+def test_backward_edges(shape, causal, d):
+    B, Hq, Hkv, N = shape
+    _say(f"[bwd] edge B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B, Hq, Hkv, N, d, seed=500 + N + d)
+    do = make_dout(q.shape, seed=900 + N + d)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = gpu_backward(q, k, v, do, scale, causal)
+    ref = attention_bwd_ref(q, k, v, do, scale, causal=causal)
+    assert_grad_parity(got, ref, f"edge {shape} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.5])
+def test_backward_other_scales(scale):
+    _say(f"[bwd] scale={scale}")
+    q, k, v = make_qkv(1, 4, 2, 200, 128, seed=71)
+    do = make_dout(q.shape, seed=72)
+    for causal in (False, True):
+        got = gpu_backward(q, k, v, do, scale, causal)
+        ref = attention_bwd_ref(q, k, v, do, scale, causal=causal)
+        if scale == 0.0:
+            # dQ and dK are exactly 0: the gradients carry a factor of scale.
+            assert not np.asarray(got[0], dtype=np.float64).any() and not np.asarray(got[1], dtype=np.float64).any()
+            x = np.asarray(got[2], dtype=np.float64)
+            err = np.abs(x - ref[2])
+            assert err.max() <= MAX_REL * np.abs(ref[2]).max() and err.mean() <= MEAN_REL * np.abs(ref[2]).mean()
+            continue
+        assert_grad_parity(got, ref, f"scale={scale} causal={causal}")
+
+
+@pytest.mark.parametrize("wid,heads", [(2, [(0, 0), (1, 31)]), (3, [(0, 0), (7, 15)])])
+def test_named_workload_backward(wid, heads):
+    """The LLaMA-7B layer shape (the backward bench line) and the spiky causal
+    prefill at full size; the oracle checks whole (batch, head) pairs."""
+    w = WORKLOADS[wid]
+    _say(f"[bwd] workload {wid} {w.name}: {w.describe()}")
+    q, k, v = make_inputs(w)
+    do = make_dout(q.shape, seed=w.seed + 7)
+    got = gpu_backward(q, k, v, do, w.scale, w.causal)
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = attention_bwd_ref(q[sl], k[sl], v[sl], do[sl], w.scale, causal=w.causal)
+        assert_grad_parity([x[sl] for x in got], ref, f"{w.name} head ({b}, {h})")
+
+
+def test_gqa_workload_backward_one_group():
+    """The GQA workload (Hq 32, Hkv 8, N 8192, d 256) at full size; the oracle
+    checks key/value head 0 (its dK, dV sum over query heads 0-3) and the dQ
+    of those four heads."""
+    w = WORKLOADS[4]
+    _say(f"[bwd] workload 4 {w.name}: {w.describe()}")
+    q, k, v = make_inputs(w)
+    do = make_dout(q.shape, seed=w.seed + 7)
+    got = gpu_backward(q, k, v, do, w.scale, w.causal)
+    ref = attention_bwd_ref(q[:, 0:4], k[:, 0:1], v[:, 0:1], do[:, 0:4], w.scale, causal=w.causal)
+    assert_grad_parity([got[0][:, 0:4], got[1][:, 0:1], got[2][:, 0:1]], ref, "gqa_causal group 0")
