@@ -34,6 +34,8 @@
 //   [CANN-FA]  www.mooersco.com/news/1200175
 //   [FA-Dict]  hwcomputing.csdn.net/6a0dbd08662f9a54cb75eb74.html
 
+#include <type_traits>
+
 #include "attn_tile.h"
 
 namespace attn {
@@ -88,6 +90,16 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(BwdParams p) {
   }
 }
 
+// Workgroup id -> work index, so that each of the 8 XCDs (one L2 each)
+// receives a contiguous range of work: the tiles of one head then share the
+// operands they all re-read in one L2 (consecutive ids go round-robin over
+// the XCDs).
+__device__ __forceinline__ int xcd_work_index() {
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3, q8 = nb >> 3, r8 = nb & 7;
+  return xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+}
+
 // Probabilities and dS of one tile from the scores s and dP, with per-entry
 // LSE (log2) and Delta: P = exp2(c s - lse2), masked entries (arg = -inf)
 // give exactly 0; dS = P (dP - delta).  Both rounded to fp16 as the B
@@ -111,6 +123,11 @@ __device__ __forceinline__ void p_and_ds(const STile<D>& arg, const STile<D>& dp
 // and dV accumulators fit in the register file next to K and V.
 template <int D>
 constexpr int bwd_dim_parts() { return D == 256 ? 2 : 1; }
+
+// dK/dV workgroups per CU the register budget allows (K, V and the two
+// accumulators stay in registers).
+template <int D>
+constexpr int bwd_dkdv_wg_per_cu() { return D == 64 ? 2 : 1; }
 
 // pv_tile over NDT of the 32-dim output tiles, whose transpose-read lane
 // offsets are in voff (the dims of those tiles only).
@@ -138,16 +155,20 @@ __device__ __forceinline__ void pv_tile_part(const char* vs, const PTile<D>& pf,
 // dO in the "V" stages); the wave's 32 keys are the columns of S and dP.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p, int k_tiles) {
+__global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dkdv_kernel(BwdParams p, int k_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-key block per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
+  // Q stages 0/1, dO stages 0/1, then per stage the tile's LSE (log2) and
+  // Delta rows (64 floats each; a 32-row tile uses the first half).
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES + 2 * 2 * 64 * 4];
+  float* const rowterms = reinterpret_cast<float*>(smem + 4 * C::TILE_BYTES);  // [stage][lse2 | delta][64]
 
   constexpr int NP = bwd_dim_parts<D>();
   constexpr int NDT = C::DT / NP;       // 32-dim output tiles of this workgroup
-  const int part = blockIdx.x % NP;
-  const int kt = (blockIdx.x / NP) % k_tiles;
-  const int bk = blockIdx.x / NP / k_tiles;   // b * Hkv + kvh
+  const int wi = xcd_work_index();
+  const int part = wi % NP;
+  const int kt = (wi / NP) % k_tiles;
+  const int bk = wi / NP / k_tiles;   // b * Hkv + kvh
   const int b = bk / p.Hkv, kvh = bk - b * p.Hkv;
   const int N = p.N;
   const int k0 = kt * kBwdKeys;
@@ -209,31 +230,45 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p,
     const uint32_t base = tile_base<D>(u < steps ? qt : 0, u < steps ? q_tiles : 0);
     load_tile<D>(qrs, k_stage<D>(smem, st), base, lo, tid);
     load_tile<D>(drs, v_stage<D>(smem, st), base, lo, tid);
+    // Waves 0 and 1 copy the tile's 64 LSE / Delta rows (4 bytes a lane);
+    // rows past the head's padded rows read as 0 and are never used.
+    if (wv < 2) {
+      const size_t rb = ((size_t)b * p.Hq + kvh * p.group + gq) * p.Npad;
+      const float* src = (wv == 0 ? p.lse2 : p.delta) + rb;
+      const __amdgpu_buffer_rsrc_t rrs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.Npad * 4, kBufferWord3);
+      const uint32_t voff = u < steps ? static_cast<uint32_t>(qt * C::BN + lane) * 4 : kSkipTile;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (lds_void*)(rowterms + (2 * st + wv) * 64), 4,
+                                               static_cast<int>(voff), 0, 0, 0);
+    }
   };
 
   issue(0, 0);
   wait_vm_all();
   __syncthreads();
-  for (int u = 0; u < steps; ++u) {
-    const int st = u & 1;
+  // One step per (query head, query tile); `stc` is the LDS stage, a
+  // compile-time constant where the loop is unrolled by two, so that the
+  // stage addresses fold into the LDS instructions' offsets.
+  auto step = [&](auto stc, int u) {
+    const int st = stc;
     const int gq = u / nq;
     const int q0 = (qt0 + (u - gq * nq)) * C::BN;
     // Causal: skip tiles whose every query precedes every key of the wave
     // (wave-uniform, as the matrix instructions need).
     const bool active = kw0 < N && !(CAUSAL && q0 + C::BN - 1 < kw0);
-    // Per-entry LSE and Delta (entry r of sub-tile t is query
-    // q0 + 32 t + 8 (r / 4) + 4 g + r % 4), loaded before the next tile's
-    // copies are queued so that waiting for them does not wait for those.
-    float lse2[C::NT][16], delta[C::NT][16];
+    issue(u + 1, st ^ 1);
     if (active) {
-      const size_t rowbase = ((size_t)b * p.Hq + kvh * p.group + gq) * p.Npad + q0;
+      // Per-entry LSE and Delta from LDS: entry r of sub-tile t is query
+      // q0 + 32 t + 8 (r / 4) + 4 g + r % 4.
+      const float* lrow = rowterms + (2 * st) * 64;
+      const float* drow = rowterms + (2 * st + 1) * 64;
+      float lse2[C::NT][16], delta[C::NT][16];
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const size_t e = rowbase + 32 * t + 8 * rr + 4 * g;
-          const float4 l4 = *reinterpret_cast<const float4*>(p.lse2 + e);
-          const float4 d4 = *reinterpret_cast<const float4*>(p.delta + e);
+          const float4 l4 = *reinterpret_cast<const float4*>(lrow + 32 * t + 8 * rr + 4 * g);
+          const float4 d4 = *reinterpret_cast<const float4*>(drow + 32 * t + 8 * rr + 4 * g);
           lse2[t][4 * rr + 0] = l4.x;
           lse2[t][4 * rr + 1] = l4.y;
           lse2[t][4 * rr + 2] = l4.z;
@@ -243,9 +278,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p,
           delta[t][4 * rr + 2] = d4.z;
           delta[t][4 * rr + 3] = d4.w;
         }
-    }
-    issue(u + 1, st ^ 1);
-    if (active) {
       STile<D> s, dp;
       qk_tile<D>(k_stage<D>(smem, st), kf, off, s);    // S = Q K^T: rows queries, columns keys
       qk_tile<D>(v_stage<D>(smem, st), vf, off, dp);   // dP = dO V^T
@@ -269,6 +301,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p,
     }
     wait_vm_all();
     __syncthreads();
+    };
+  if constexpr (D == 64) {
+    // Unrolled, this head_dim no longer fits two workgroups per CU.
+    for (int u = 0; u < steps; ++u) step(u & 1, u);
+  } else {
+    for (int u = 0; u < steps; u += 2) {
+      step(std::integral_constant<int, 0>{}, u);
+      if (u + 1 < steps) step(std::integral_constant<int, 1>{}, u + 1);
+    }
   }
 
   if (key >= N) return;
@@ -295,13 +336,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p,
 // the lanes' columns), K and V tiles stream through LDS.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(BwdParams p, int q_tiles) {
+__global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_bwd_dq_kernel(BwdParams p, int q_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-row block per wave");
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
 
-  int qt = blockIdx.x % q_tiles;
-  const int bh = blockIdx.x / q_tiles;   // b * Hq + hq
+  const int wi = xcd_work_index();
+  int qt = wi % q_tiles;
+  const int bh = wi / q_tiles;   // b * Hq + hq
   if (CAUSAL) qt = q_tiles - 1 - qt;     // heaviest tiles first
   const int b = bh / p.Hq, hq = bh - b * p.Hq, kvh = hq / p.group;
   const int N = p.N;
@@ -356,8 +398,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(BwdParams p, i
   load_tile<D>(vrs, v_stage<D>(smem, 0), 0, lo, tid);
   wait_vm_all();
   __syncthreads();
-  for (int j = 0; j < nt; ++j) {
-    const int st = j & 1;
+  // One key tile per step; the stage is a compile-time constant in the
+  // loop unrolled by two (see the dK/dV kernel).
+  auto step = [&](auto stc, int j) {
+    const int st = stc;
     const uint32_t nb = tile_base<D>(j + 1, nt);
     load_tile<D>(krs, k_stage<D>(smem, st ^ 1), nb, lo, tid);
     load_tile<D>(vrs, v_stage<D>(smem, st ^ 1), nb, lo, tid);
@@ -382,6 +426,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(BwdParams p, i
     }
     wait_vm_all();
     __syncthreads();
+    };
+  if constexpr (D == 128) {
+    // Unrolled, this head_dim no longer fits two workgroups per CU.
+    for (int j = 0; j < nt; ++j) step(j & 1, j);
+  } else {
+    for (int j = 0; j < nt; j += 2) {
+      step(std::integral_constant<int, 0>{}, j);
+      if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
+    }
   }
 
   if (row >= N) return;
