@@ -21,7 +21,7 @@ ATTN_ERR_INVALID_ARG = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_DEVICE = 3
 
-EXPORTS = ("attn_fwd", "attn_check_args", "attn_decode", "attn_decode_workspace_size",
+EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_check_args", "attn_decode", "attn_decode_workspace_size",
            "attn_check_decode_args", "attn_bwd", "attn_bwd_workspace_size", "attn_check_bwd_args",
            "attn_status_string", "attn_version")
 
@@ -59,6 +59,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                              ctypes.c_float, ctypes.c_int, vp]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_bf16.argtypes = lib.attn_fwd.argtypes
+    lib.attn_fwd_bf16.restype = ctypes.c_int
     lib.attn_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float]
     lib.attn_check_args.restype = ctypes.c_int
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
@@ -112,21 +114,23 @@ def _raise_for(status: int):
 
 def attn_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, out=None,
              lse=None, return_lse: bool = True, stream=None):
-    """Fused attention forward on torch fp16 tensors resident on one AMD GPU.
+    """Fused attention forward on torch fp16 or bf16 tensors resident on one AMD GPU.
 
-    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous torch.float16 on the
-    same HIP device.  scale defaults to 1/sqrt(d).  Returns (o, lse) with o
+    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous torch.float16 (or all
+    torch.bfloat16) on the same HIP device; o has the same type.  scale defaults to 1/sqrt(d).  Returns (o, lse) with o
     [B, Hq, N, d] fp16 and lse [B, Hq, N] fp32 (None if return_lse is False
     and no lse buffer is given).  The kernel is queued on ``stream`` (a
     torch.cuda.Stream) or on torch's current stream of q's device.
     """
     import torch
 
+    if not isinstance(q, torch.Tensor) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("q must be a torch.float16 or torch.bfloat16 tensor")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.float16:
-            raise TypeError(f"{name} must be torch.float16, got {t.dtype}")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype {q.dtype}, got {t.dtype}")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be on an AMD GPU (torch 'cuda' device), got {t.device}")
         if t.dim() != 4:
@@ -144,9 +148,9 @@ def attn_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, out=N
 
     if out is None:
         out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != torch.float16 or out.device != q.device
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
           or not out.is_contiguous()):
-        raise ValueError("out must be a contiguous fp16 tensor shaped like q on q's device")
+        raise ValueError("out must be a contiguous tensor of q's dtype, shaped like q on q's device")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     elif lse is not None and (lse.shape != (B, Hq, N) or lse.dtype != torch.float32
@@ -156,7 +160,8 @@ def attn_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, out=N
     lib = load_library()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        status = lib.attn_fwd(
+        fn = lib.attn_fwd_bf16 if q.dtype == torch.bfloat16 else lib.attn_fwd
+        status = fn(
             q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
             out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
             B, Hq, Hkv, N, d, float(scale), 1 if causal else 0, s.cuda_stream or None)

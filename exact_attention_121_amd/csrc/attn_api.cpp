@@ -70,9 +70,10 @@ extern "C" int attn_check_args(const void* q, const void* k, const void* v, cons
   return ATTN_OK;
 }
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
-                        int causal, struct ihipStream_t* stream) {
+namespace {
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+               int64_t Hkv, int64_t N, int64_t d, float scale, int causal, int bf16, struct ihipStream_t* stream) {
   const int st = attn_check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
   if (st != ATTN_OK) return st;
   if (B == 0 || N == 0) return ATTN_OK;
@@ -89,7 +90,22 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   a.d = static_cast<int>(d);
   a.scale = scale;
   a.causal = causal != 0;
+  a.bf16 = bf16;
   return attn::launch_forward(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
+                        int causal, struct ihipStream_t* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 0, stream);
+}
+
+extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
+                             int causal, struct ihipStream_t* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 1, stream);
 }
 
 namespace {
@@ -273,4 +289,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" const char* attn_version(void) { return "attn_fwd 0.3.0 gfx950"; }
+extern "C" const char* attn_version(void) { return "attn_fwd 0.3.1 gfx950"; }

@@ -11,6 +11,9 @@
 // with the normalisation deferred to the end ([CANN-FA], the paragraph on the
 // online softmax being the key; [FA-Dict] section "Online softmax").
 //
+// The element type of Q, K, V and O is fp16 (the pages' precision) or bf16;
+// P takes the same type for the P.V product, all accumulation is fp32.
+//
 // Pages cited:
 //   [CANN-FA]  www.mooersco.com/news/1200175 - "FlashAttention operator of the
 //              CANN ops-transformer repository: attention acceleration on the
@@ -75,7 +78,7 @@ struct Params {
   uint32_t q_keep;  // 0 when scale = 0 (every logit is then exactly 0), else all ones
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T>
 __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
   // K stages 0/1 then V stages 0/1.
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_fwd_kernel(P
   // Prologue: logits of tile 0 and the first running max.
   STile<D> sa, sb;
   if (w.nt_w > 0) {
-    qk_tile<D>(k_stage<D>(smem, 0), w.qf, w.off, sa);
+    qk_tile<D, T>(k_stage<D>(smem, 0), w.qf, w.off, sa);
     if (C::BN > N || (CAUSAL && C::BN - 1 > w.qw0)) mask_tile<D, CAUSAL>(sa, 0, N, w.qrow, w.g);
     // Key 0 is visible to every row, so these maxima are finite.
     tile_max<D>(sa, w.c, w.m_run);
@@ -167,8 +170,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_fwd_kernel(P
   __syncthreads();
 
   for (int j = 0; j < nt; j += 2) {
-    pipeline_step<D, CAUSAL, 0>(j, nt, smem, krs, vrs, lo, tid, w, sa, sb);
-    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1>(j + 1, nt, smem, krs, vrs, lo, tid, w, sb, sa);
+    pipeline_step<D, CAUSAL, 0, T>(j, nt, smem, krs, vrs, lo, tid, w, sa, sb);
+    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1, T>(j + 1, nt, smem, krs, vrs, lo, tid, w, sb, sa);
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_fwd_kernel(P
         for (int rq = 0; rq < 4; ++rq) {
           half4 h;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(w.oacc[qb][dt][4 * rq + i] * inv);
+          for (int i = 0; i < 4; ++i) h[i] = to_elem<T>(w.oacc[qb][dt][4 * rq + i] * inv);
           *reinterpret_cast<half4*>(orow + 32 * dt + 8 * rq + 4 * w.g) = h;
         }
       if (p.lse != nullptr && w.g == 0)
@@ -198,7 +201,10 @@ template <int D, bool CAUSAL>
 hipError_t launch_t(const LaunchArgs& a, Params p, hipStream_t s) {
   p.q_tiles = (a.N + Cfg<D>::BM - 1) / Cfg<D>::BM;
   const unsigned grid = static_cast<unsigned>(a.B) * a.Hq * p.q_tiles;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, s, p);
+  if (a.bf16)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, __bf16>), dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, _Float16>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

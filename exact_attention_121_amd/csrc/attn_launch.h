@@ -18,6 +18,7 @@ struct LaunchArgs {
   int B, Hq, Hkv, N, d;
   float scale;
   int causal;
+  int bf16;    // element type of q, k, v, o: 0 = fp16, 1 = bf16
 };
 
 // Queues the fused forward kernel on `stream` (a hipStream_t).  Returns the

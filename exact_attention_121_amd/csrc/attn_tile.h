@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_launch.h"
 
 namespace attn {
@@ -25,6 +27,8 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -186,10 +190,31 @@ using OAcc = f32x16[Cfg<D>::QB][Cfg<D>::DT];  // output accumulators O^T
 template <int D>
 using QFrag = half8[Cfg<D>::QB][Cfg<D>::DC];  // Q rows as B operands
 
+// Element type T of Q, K, V, O and of P in the P.V product: _Float16 or
+// __bf16.  Fragments are held as 8 x 16-bit vectors (half8) for either type
+// and reinterpreted for the matrix instruction; to_elem rounds an fp32 value
+// to T (to nearest even) and returns its 16 bits.
+template <typename T>
+__device__ __forceinline__ f32x16 mfma16(half8 a, half8 b, f32x16 c) {
+  if constexpr (std::is_same_v<T, __bf16>)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ _Float16 to_elem(float x) {
+  if constexpr (std::is_same_v<T, __bf16>)
+    return __builtin_bit_cast(_Float16, static_cast<__bf16>(x));
+  else
+    return static_cast<_Float16>(x);
+}
+
 // S^T = K Q^T for one key tile: s[qb][t] holds keys 32 t .. 32 t + 31 (rows
 // of the 32x32 result) against query block qb (columns).  Each K operand
 // read from LDS serves every query block of the wave.
-template <int D>
+template <int D, typename T = _Float16>
 __device__ __forceinline__ void qk_tile(const char* ks, const QFrag<D>& qf, const Offsets<D>& off,
                                         STile<D>& s) {
   using C = Cfg<D>;
@@ -204,7 +229,7 @@ __device__ __forceinline__ void qk_tile(const char* ks, const QFrag<D>& qf, cons
       const half8 a = *reinterpret_cast<const half8*>(ks + off.k[dc] + 32 * t * C::CPR * 16);
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
-        s[qb][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[qb][dc], s[qb][t], 0, 0, 0);
+        s[qb][t] = mfma16<T>(a, qf[qb][dc], s[qb][t]);
     }
 }
 
@@ -268,7 +293,7 @@ __device__ __forceinline__ void raise_max(const float (&m_tile)[Cfg<D>::QB], flo
 
 // P = exp2(c S - m) rounded to fp16: the B operand of the P.V product, in
 // the lane's own key order.
-template <int D>
+template <int D, typename T = _Float16>
 __device__ __forceinline__ void softmax_tile(const STile<D>& s, float c, const float (&m_run)[Cfg<D>::QB],
                                              PTile<D>& pf) {
   using C = Cfg<D>;
@@ -279,12 +304,12 @@ __device__ __forceinline__ void softmax_tile(const STile<D>& s, float c, const f
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         pf[qb][t][r >> 3][r & 7] =
-            static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][t][r], c, -m_run[qb])));
+            to_elem<T>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][t][r], c, -m_run[qb])));
 }
 
 // Adds the sum of the fp16 probabilities (exactly the values multiplied
 // into V) to the lane's partial row sums l.
-template <int D>
+template <int D, typename T = _Float16>
 __device__ __forceinline__ void add_row_sums(const PTile<D>& pf, float (&l_run)[Cfg<D>::QB]) {
   using C = Cfg<D>;
 #pragma unroll
@@ -296,10 +321,19 @@ __device__ __forceinline__ void add_row_sums(const PTile<D>& pf, float (&l_run)[
       for (int h = 0; h < 2; ++h)
       {
         const half8 x = pf[qb][t][h];
-        l0 = __builtin_amdgcn_fdot2(half2v{x[0], x[1]}, half2v{1.0f16, 1.0f16}, l0, false);
-        l1 = __builtin_amdgcn_fdot2(half2v{x[2], x[3]}, half2v{1.0f16, 1.0f16}, l1, false);
-        l0 = __builtin_amdgcn_fdot2(half2v{x[4], x[5]}, half2v{1.0f16, 1.0f16}, l0, false);
-        l1 = __builtin_amdgcn_fdot2(half2v{x[6], x[7]}, half2v{1.0f16, 1.0f16}, l1, false);
+        if constexpr (std::is_same_v<T, __bf16>) {
+          const bf16x8 y = __builtin_bit_cast(bf16x8, x);
+          const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{y[0], y[1]}, one, l0, false);
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{y[2], y[3]}, one, l1, false);
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{y[4], y[5]}, one, l0, false);
+          l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{y[6], y[7]}, one, l1, false);
+        } else {
+          l0 = __builtin_amdgcn_fdot2(half2v{x[0], x[1]}, half2v{1.0f16, 1.0f16}, l0, false);
+          l1 = __builtin_amdgcn_fdot2(half2v{x[2], x[3]}, half2v{1.0f16, 1.0f16}, l1, false);
+          l0 = __builtin_amdgcn_fdot2(half2v{x[4], x[5]}, half2v{1.0f16, 1.0f16}, l0, false);
+          l1 = __builtin_amdgcn_fdot2(half2v{x[6], x[7]}, half2v{1.0f16, 1.0f16}, l1, false);
+        }
       }
     l_run[qb] += l0 + l1;
   }
@@ -309,7 +343,7 @@ __device__ __forceinline__ void add_row_sums(const PTile<D>& pf, float (&l_run)[
 // group g with key 8 (j/4) + 4 g + j%4 (+16 h, +32 t): two transpose reads of
 // four keys each from V in its natural [key][dim] layout, shared by every
 // query block of the wave.
-template <int D>
+template <int D, typename T = _Float16>
 __device__ __forceinline__ void pv_tile(const char* vs, const PTile<D>& pf, const Offsets<D>& off,
                                         OAcc<D>& oacc) {
   using C = Cfg<D>;
@@ -325,7 +359,7 @@ __device__ __forceinline__ void pv_tile(const char* vs, const PTile<D>& pf, cons
         const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb)
-          oacc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[qb][t][h], oacc[qb][dt], 0, 0, 0);
+          oacc[qb][dt] = mfma16<T>(a, pf[qb][t][h], oacc[qb][dt]);
       }
     }
 }
@@ -360,7 +394,7 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kS
 // V_{j+1} and K_{j+2} stream into the stages freed by the previous iteration
 // ([CANN-FA] section "Ascend C implementation": load the next block while the
 // current one is computed).
-template <int D, bool CAUSAL, int PAR>
+template <int D, bool CAUSAL, int PAR, typename T = _Float16>
 __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                               const LoadOffsets<D>& lo, int tid, WaveState<D>& w,
@@ -374,9 +408,9 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
     // S_{j+1} is computed even past this wave's last tile (reading a stale
     // but in-bounds stage) so that the matrix and vector work stay in one
     // block the scheduler can interleave; it is discarded then.
-    qk_tile<D>(k_stage<D>(smem, PAR ^ 1), w.qf, w.off, s_nxt);
+    qk_tile<D, T>(k_stage<D>(smem, PAR ^ 1), w.qf, w.off, s_nxt);
     PTile<D> pf;
-    softmax_tile<D>(s_cur, w.c, w.m_run, pf);
+    softmax_tile<D, T>(s_cur, w.c, w.m_run, pf);
     // Materialise P_j here, so that the compiler keeps the softmax next to
     // the S_{j+1} product instead of sinking it past the mask branch.
 #pragma unroll
@@ -407,8 +441,8 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
     // P_j V_j, so that the other wave of the SIMD fills the gaps with its
     // vector work rather than the reverse.
     __builtin_amdgcn_s_setprio(1);
-    pv_tile<D>(v_stage<D>(smem, PAR), pf, w.off, w.oacc);
-    add_row_sums<D>(pf, w.l_run);
+    pv_tile<D, T>(v_stage<D>(smem, PAR), pf, w.off, w.oacc);
+    add_row_sums<D, T>(pf, w.l_run);
     float m_tile[C::QB];
     tile_max<D>(s_nxt, w.c, m_tile);
     if constexpr (C::DC >= 8) {

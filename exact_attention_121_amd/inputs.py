@@ -16,6 +16,8 @@ Recipe (every draw uses numpy's PCG64 ``default_rng``):
     are {0, N-1} plus R-2 distinct rows drawn uniformly without replacement
     from 1..N-2 by ``default_rng(seed + 10**6 + b*Hq + hq)``, sorted.
 
+  * bf16 inputs: the same draws, rounded to bfloat16 (to nearest even)
+    instead of fp16.
   * Decode inputs: Q [B, Hq, Nq, d] is drawn first, then K and V
     [B, Hkv, Nk, d], each as above (one head at a time, N(0, sigma^2)).
 
@@ -118,6 +120,35 @@ def make_qkv(B, Hq, Hkv, N, d, seed, sigma=1.0, spike_frac=0.0, spike_mult=1.0):
     k = _draw(rng, B, Hkv, N, d, sigma, spike_frac, spike_mult)
     v = _draw(rng, B, Hkv, N, d, sigma, 0.0, 1.0)
     return q, k, v
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bfloat16 (ties to even), returned as
+    fp32 (every bf16 value is exactly an fp32 value).  NaN/Inf are not drawn."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bits = (bits + (np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return bits.view(np.float32)
+
+
+def make_qkv_bf16(B, Hq, Hkv, N, d, seed, sigma=1.0, spike_frac=0.0, spike_mult=1.0):
+    """Q, K, V as make_qkv draws them (same generator calls), rounded to
+    bfloat16 instead of fp16; fp32 arrays holding bf16 values."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for H, spiky in ((Hq, True), (Hkv, True), (Hkv, False)):
+        full = np.empty((B, H, N, d), dtype=np.float32)
+        for b in range(B):
+            for h in range(H):
+                x = rng.standard_normal((N, d), dtype=np.float32)
+                if sigma != 1.0:
+                    x *= np.float32(sigma)
+                full[b, h] = x
+        if spiky and spike_frac > 0.0:
+            count = int(round(spike_frac * B * H * N))
+            rows = rng.choice(B * H * N, size=count, replace=False)
+            full.reshape(B * H * N, d)[rows] *= np.float32(spike_mult)
+        out.append(round_to_bf16(full))
+    return tuple(out)
 
 
 def make_inputs(w: Workload, seed: int | None = None):

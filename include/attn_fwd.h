@@ -96,6 +96,17 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              float scale, int causal, struct ihipStream_t* stream);
 
 /*
+ * attn_fwd_bf16 - attn_fwd for bfloat16 q, k, v and o (same arguments,
+ * layout, limits and status codes; lse stays fp32).  The pages use fp16
+ * ([CANN-FA] section "Performance vs standard attention"); bf16 is the
+ * other 16-bit type models are trained in.  P is rounded to bf16 for the
+ * P.V product, every sum is fp32, O is rounded to bf16 (to nearest even).
+ */
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                  float scale, int causal, struct ihipStream_t* stream);
+
+/*
  * attn_check_args - the argument validation of attn_fwd, on the host only.
  * Pointers are compared with NULL and with each other's address ranges but
  * never dereferenced; no HIP call is made, so it runs without a GPU.

@@ -66,3 +66,17 @@ def test_sample_rows():
     assert np.array_equal(r, sample_rows(w))
     small = sample_rows(WORKLOADS[1], count=1000)
     assert np.array_equal(small[0, 0], np.arange(128))
+
+
+def test_bf16_rounding_matches_torch():
+    """round_to_bf16 is round-to-nearest-even to bfloat16: torch's own fp32 ->
+    bf16 conversion gives the same values (ties included)."""
+    import numpy as np
+    import torch
+
+    from exact_attention_121_amd.inputs import round_to_bf16
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 10.0 ** rng.integers(-8, 8, 20000),
+                        # exact ties between two bf16 values, both parities
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.0 - 2.0 ** -7, 0.0], np.float32)])
+    assert np.array_equal(round_to_bf16(x), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
