@@ -21,8 +21,8 @@ ATTN_ERR_INVALID_ARG = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_DEVICE = 3
 
-EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_check_args", "attn_decode", "attn_decode_workspace_size",
-           "attn_check_decode_args", "attn_bwd", "attn_bwd_workspace_size", "attn_check_bwd_args",
+EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_check_args", "attn_decode", "attn_decode_bf16", "attn_decode_workspace_size",
+           "attn_check_decode_args", "attn_bwd", "attn_bwd_bf16", "attn_bwd_workspace_size", "attn_check_bwd_args",
            "attn_status_string", "attn_version")
 
 _lib = None
@@ -66,6 +66,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                                 ctypes.c_int, vp, i64, vp]
     lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_bf16.argtypes = lib.attn_decode.argtypes
+    lib.attn_decode_bf16.restype = ctypes.c_int
     lib.attn_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]
     lib.attn_decode_workspace_size.restype = ctypes.c_int
     lib.attn_check_decode_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
@@ -74,6 +76,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                              ctypes.c_int, vp, i64, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_bf16.argtypes = lib.attn_bwd.argtypes
+    lib.attn_bwd_bf16.restype = ctypes.c_int
     lib.attn_bwd_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64)]
     lib.attn_bwd_workspace_size.restype = ctypes.c_int
     lib.attn_check_bwd_args.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
@@ -184,7 +188,7 @@ def attn_check_decode_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, worksp
 
 def attn_decode(q, k, v, *, scale: float | None = None, causal: bool = True, out=None, lse=None,
                 return_lse: bool = True, workspace=None, stream=None):
-    """Decode step on torch fp16 tensors: q [B, Hq, Nq, d] are the last Nq
+    """Decode step on torch fp16 (or bf16) tensors: q [B, Hq, Nq, d] are the last Nq
     positions of a sequence whose keys/values k, v [B, Hkv, Nk, d] are
     cached (Nq <= Nk).  With causal, query i sees keys 0 .. Nk - Nq + i.
     ``workspace`` is an optional uint8 device tensor of at least
@@ -193,11 +197,13 @@ def attn_decode(q, k, v, *, scale: float | None = None, causal: bool = True, out
     """
     import torch
 
+    if not isinstance(q, torch.Tensor) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("q must be a torch.float16 or torch.bfloat16 tensor")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.float16:
-            raise TypeError(f"{name} must be torch.float16, got {t.dtype}")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype {q.dtype}, got {t.dtype}")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be on an AMD GPU (torch 'cuda' device), got {t.device}")
         if t.dim() != 4:
@@ -214,9 +220,9 @@ def attn_decode(q, k, v, *, scale: float | None = None, causal: bool = True, out
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != torch.float16 or out.device != q.device
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
           or not out.is_contiguous()):
-        raise ValueError("out must be a contiguous fp16 tensor shaped like q on q's device")
+        raise ValueError("out must be a contiguous tensor of q's dtype, shaped like q on q's device")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     elif lse is not None and (lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32
@@ -232,7 +238,8 @@ def attn_decode(q, k, v, *, scale: float | None = None, causal: bool = True, out
     lib = load_library()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        status = lib.attn_decode(
+        fn = lib.attn_decode_bf16 if q.dtype == torch.bfloat16 else lib.attn_decode
+        status = fn(
             q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
             out.data_ptr() or None, (lse.data_ptr() or None) if lse is not None else None,
             B, Hq, Hkv, Nq, Nk, d, float(scale), 1 if causal else 0,
@@ -259,7 +266,7 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool 
              dv=None, workspace=None, stream=None):
     """Attention backward on torch tensors resident on one AMD GPU.
 
-    q, o, dout: [B, Hq, N, d] fp16 and k, v: [B, Hkv, N, d] fp16, with o and
+    q, o, dout: [B, Hq, N, d] and k, v: [B, Hkv, N, d], all fp16 or all bf16, with o and
     lse ([B, Hq, N] fp32) as attn_fwd returned them for the same q, k, v,
     scale and causal.  Returns (dq, dk, dv) shaped like q, k, v.
     ``workspace`` is an optional uint8 device tensor of at least
@@ -267,11 +274,13 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool 
     """
     import torch
 
+    if not isinstance(q, torch.Tensor) or q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("q must be a torch.float16 or torch.bfloat16 tensor")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.float16:
-            raise TypeError(f"{name} must be torch.float16, got {t.dtype}")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype {q.dtype}, got {t.dtype}")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be on an AMD GPU (torch 'cuda' device), got {t.device}")
         if t.dim() != 4:
@@ -295,9 +304,9 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool 
     for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t is None:
             t = torch.empty_like(like)
-        elif (t.shape != like.shape or t.dtype != torch.float16 or t.device != q.device
+        elif (t.shape != like.shape or t.dtype != q.dtype or t.device != q.device
               or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous fp16 tensor shaped like its input")
+            raise ValueError(f"{name} must be a contiguous tensor of q's dtype shaped like its input")
         outs.append(t)
     dq, dk, dv = outs
     need = attn_bwd_workspace_size(B, Hq, N, d)
@@ -310,7 +319,8 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool 
     lib = load_library()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        status = lib.attn_bwd(
+        fn = lib.attn_bwd_bf16 if q.dtype == torch.bfloat16 else lib.attn_bwd
+        status = fn(
             q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
             lse.data_ptr() or None, dout.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
             dv.data_ptr() or None, B, Hq, Hkv, N, d, float(scale), 1 if causal else 0,

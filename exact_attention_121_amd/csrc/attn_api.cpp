@@ -166,9 +166,11 @@ extern "C" int attn_check_decode_args(const void* q, const void* k, const void* 
   return ATTN_OK;
 }
 
-extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                           int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
-                           void* workspace, int64_t workspace_bytes, struct ihipStream_t* stream) {
+namespace {
+
+int decode_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                  int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, void* workspace,
+                  int64_t workspace_bytes, int bf16, struct ihipStream_t* stream) {
   const int st = attn_check_decode_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, workspace,
                                         workspace_bytes);
   if (st != ATTN_OK) return st;
@@ -188,8 +190,23 @@ extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o,
   a.d = static_cast<int>(d);
   a.scale = scale;
   a.causal = causal != 0;
+  a.bf16 = bf16;
   a.plan = attn::decode_plan(B, Hq, Hkv, Nq, Nk, d);
   return attn::launch_decode(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                           int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                           void* workspace, int64_t workspace_bytes, struct ihipStream_t* stream) {
+  return decode_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes, 0, stream);
+}
+
+extern "C" int attn_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                                void* workspace, int64_t workspace_bytes, struct ihipStream_t* stream) {
+  return decode_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes, 1, stream);
 }
 
 extern "C" int attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t N, int64_t d, int64_t* bytes) {
@@ -245,10 +262,11 @@ extern "C" int attn_check_bwd_args(const void* q, const void* k, const void* v, 
   return ATTN_OK;
 }
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                        const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
-                        int64_t N, int64_t d, float scale, int causal, void* workspace, int64_t workspace_bytes,
-                        struct ihipStream_t* stream) {
+namespace {
+
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
+               int causal, void* workspace, int64_t workspace_bytes, int bf16, struct ihipStream_t* stream) {
   const int st = attn_check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace,
                                      workspace_bytes);
   if (st != ATTN_OK) return st;
@@ -271,7 +289,26 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   a.d = static_cast<int>(d);
   a.scale = scale;
   a.causal = causal != 0;
+  a.bf16 = bf16;
   return attn::launch_backward(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                        int64_t N, int64_t d, float scale, int causal, void* workspace, int64_t workspace_bytes,
+                        struct ihipStream_t* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, workspace, workspace_bytes,
+                    0, stream);
+}
+
+extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                             int64_t N, int64_t d, float scale, int causal, void* workspace,
+                             int64_t workspace_bytes, struct ihipStream_t* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, workspace, workspace_bytes,
+                    1, stream);
 }
 
 extern "C" const char* attn_status_string(int status) {

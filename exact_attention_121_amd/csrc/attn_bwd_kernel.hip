@@ -1,5 +1,6 @@
 // Fused attention backward for gfx950: dQ, dK, dV from Q, K, V, the
-// forward's O and LSE, and the upstream gradient dO.
+// forward's O and LSE, and the upstream gradient dO, in fp16 or bf16 (P and
+// dS take the same type for the products that use them; sums are fp32).
 //
 // The pages name training as a use of the operator ([CANN-FA], opening
 // paragraph) and note that backpropagation must keep gradients ([FA-Dict]
@@ -43,6 +44,15 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The 16 bits of an element of type T (fp16 or bf16) as fp32 (exact).
+template <typename T>
+__device__ __forceinline__ float from_elem(_Float16 bits) {
+  if constexpr (std::is_same_v<T, __bf16>)
+    return static_cast<float>(__builtin_bit_cast(__bf16, bits));
+  else
+    return static_cast<float>(bits);
+}
+
 struct BwdParams {
   const _Float16* q;
   const _Float16* k;
@@ -64,7 +74,7 @@ struct BwdParams {
 // Delta and LSE in log2 units.  D / 8 lanes per row (16-byte loads), the
 // row's partial dot products summed with lane shuffles.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(BwdParams p) {
   constexpr int CH = D / 8;                 // lanes per row
   constexpr int ROWS = kThreads / CH;       // rows per workgroup
@@ -80,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(BwdParams p) {
     const half8 a = *reinterpret_cast<const half8*>(p.o + off);
     const half8 g = *reinterpret_cast<const half8*>(p.dout + off);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += static_cast<float>(a[e]) * static_cast<float>(g[e]);
+    for (int e = 0; e < 8; ++e) acc += from_elem<T>(a[e]) * from_elem<T>(g[e]);
   }
 #pragma unroll
   for (int w = CH / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
@@ -104,7 +114,7 @@ __device__ __forceinline__ int xcd_work_index() {
 // LSE (log2) and Delta: P = exp2(c s - lse2), masked entries (arg = -inf)
 // give exactly 0; dS = P (dP - delta).  Both rounded to fp16 as the B
 // operands of the following products (the forward's P layout).
-template <int D>
+template <int D, typename T>
 __device__ __forceinline__ void p_and_ds(const STile<D>& arg, const STile<D>& dp, const float (&delta)[Cfg<D>::NT][16],
                                          PTile<D>& pf, PTile<D>& dsf) {
   using C = Cfg<D>;
@@ -113,8 +123,8 @@ __device__ __forceinline__ void p_and_ds(const STile<D>& arg, const STile<D>& dp
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float pv = __builtin_amdgcn_exp2f(arg[0][t][r]);
-      pf[0][t][r >> 3][r & 7] = static_cast<_Float16>(pv);
-      dsf[0][t][r >> 3][r & 7] = static_cast<_Float16>(pv * (dp[0][t][r] - delta[t][r]));
+      pf[0][t][r >> 3][r & 7] = to_elem<T>(pv);
+      dsf[0][t][r >> 3][r & 7] = to_elem<T>(pv * (dp[0][t][r] - delta[t][r]));
     }
 }
 
@@ -131,7 +141,7 @@ constexpr int bwd_dkdv_wg_per_cu() { return D == 64 ? 2 : 1; }
 
 // pv_tile over NDT of the 32-dim output tiles, whose transpose-read lane
 // offsets are in voff (the dims of those tiles only).
-template <int D, int NDT>
+template <int D, int NDT, typename T>
 __device__ __forceinline__ void pv_tile_part(const char* vs, const PTile<D>& pf, const int (&voff)[2][NDT],
                                              f32x16 (&acc)[NDT]) {
   using C = Cfg<D>;
@@ -145,7 +155,7 @@ __device__ __forceinline__ void pv_tile_part(const char* vs, const PTile<D>& pf,
         const short4v lo = tr_read(vs + voff[0][i] + kb);
         const short4v hi = tr_read(vs + voff[1][i] + kb);
         const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[0][t][h], acc[i], 0, 0, 0);
+        acc[i] = mfma16<T>(a, pf[0][t][h], acc[i]);
       }
     }
 }
@@ -154,7 +164,7 @@ __device__ __forceinline__ void pv_tile_part(const char* vs, const PTile<D>& pf,
 // dK, dV.  Query tiles of BN rows stream through LDS (Q in the "K" stages,
 // dO in the "V" stages); the wave's 32 keys are the columns of S and dP.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T>
 __global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dkdv_kernel(BwdParams p, int k_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-key block per wave");
@@ -279,8 +289,8 @@ __global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dk
           delta[t][4 * rr + 3] = d4.w;
         }
       STile<D> s, dp;
-      qk_tile<D>(k_stage<D>(smem, st), kf, off, s);    // S = Q K^T: rows queries, columns keys
-      qk_tile<D>(v_stage<D>(smem, st), vf, off, dp);   // dP = dO V^T
+      qk_tile<D, T>(k_stage<D>(smem, st), kf, off, s);    // S = Q K^T: rows queries, columns keys
+      qk_tile<D, T>(v_stage<D>(smem, st), vf, off, dp);   // dP = dO V^T
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
 #pragma unroll
@@ -295,9 +305,9 @@ __global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dk
           }
       }
       PTile<D> pf, dsf;
-      p_and_ds<D>(s, dp, delta, pf, dsf);
-      pv_tile_part<D, NDT>(v_stage<D>(smem, st), pf, voff, dv_acc);    // dV^T += dO^T P
-      pv_tile_part<D, NDT>(k_stage<D>(smem, st), dsf, voff, dk_acc);   // dK^T += Q^T dS
+      p_and_ds<D, T>(s, dp, delta, pf, dsf);
+      pv_tile_part<D, NDT, T>(v_stage<D>(smem, st), pf, voff, dv_acc);    // dV^T += dO^T P
+      pv_tile_part<D, NDT, T>(k_stage<D>(smem, st), dsf, voff, dk_acc);   // dK^T += Q^T dS
     }
     wait_vm_all();
     __syncthreads();
@@ -322,8 +332,8 @@ __global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dk
       half4 hk, hv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hk[e] = static_cast<_Float16>(dk_acc[i][4 * rq + e] * p.scale);
-        hv[e] = static_cast<_Float16>(dv_acc[i][4 * rq + e]);
+        hk[e] = to_elem<T>(dk_acc[i][4 * rq + e] * p.scale);
+        hv[e] = to_elem<T>(dv_acc[i][4 * rq + e]);
       }
       const int dim0 = 32 * (part * NDT + i) + 8 * rq + 4 * g;
       *reinterpret_cast<half4*>(dkrow + dim0) = hk;
@@ -335,7 +345,7 @@ __global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dk
 // dQ.  Like the forward kernel: 128 query rows per workgroup (32 per wave,
 // the lanes' columns), K and V tiles stream through LDS.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T>
 __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_bwd_dq_kernel(BwdParams p, int q_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-row block per wave");
@@ -407,8 +417,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_bwd_dq_kerne
     load_tile<D>(vrs, v_stage<D>(smem, st ^ 1), nb, lo, tid);
     if (j < nt_w) {
       STile<D> s, dp;
-      qk_tile<D>(k_stage<D>(smem, st), qf, off, s);    // S^T = K Q^T
-      qk_tile<D>(v_stage<D>(smem, st), df, off, dp);   // dP^T = V dO^T
+      qk_tile<D, T>(k_stage<D>(smem, st), qf, off, s);    // S^T = K Q^T
+      qk_tile<D, T>(v_stage<D>(smem, st), df, off, dp);   // dP^T = V dO^T
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
 #pragma unroll
@@ -421,8 +431,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_bwd_dq_kerne
 #pragma unroll
         for (int r = 0; r < 16; ++r) dl[t][r] = delta;
       PTile<D> pf, dsf;
-      p_and_ds<D>(s, dp, dl, pf, dsf);
-      pv_tile<D>(k_stage<D>(smem, st), dsf, off, dq_acc);   // dQ^T += K^T dS^T
+      p_and_ds<D, T>(s, dp, dl, pf, dsf);
+      pv_tile<D, T>(k_stage<D>(smem, st), dsf, off, dq_acc);   // dQ^T += K^T dS^T
     }
     wait_vm_all();
     __syncthreads();
@@ -445,27 +455,27 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_bwd_dq_kerne
     for (int rq = 0; rq < 4; ++rq) {
       half4 h;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(dq_acc[0][dt][4 * rq + i] * p.scale);
+      for (int i = 0; i < 4; ++i) h[i] = to_elem<T>(dq_acc[0][dt][4 * rq + i] * p.scale);
       *reinterpret_cast<half4*>(out + 32 * dt + 8 * rq + 4 * g) = h;
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T>
 hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   using C = Cfg<D>;
   constexpr int rows_per_wg = kThreads / (D / 8);
   const unsigned prep_grid = static_cast<unsigned>((p.rows_total + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((attn_bwd_prep_kernel<D>), dim3(prep_grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<D, T>), dim3(prep_grid), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int k_tiles = (a.N + kBwdKeys - 1) / kBwdKeys;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>),
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, T>),
                      dim3(static_cast<unsigned>(a.B) * a.Hkv * k_tiles * bwd_dim_parts<D>()), dim3(kThreads), 0, s,
                      p, k_tiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int q_tiles = (a.N + C::BM - 1) / C::BM;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(static_cast<unsigned>(a.B) * a.Hq * q_tiles),
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, T>), dim3(static_cast<unsigned>(a.B) * a.Hq * q_tiles),
                      dim3(kThreads), 0, s, p, q_tiles);
   return hipGetLastError();
 }
@@ -495,15 +505,24 @@ int launch_backward(const BwdArgs& a, void* stream) {
   p.scale = a.scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  switch (a.d) {
-    case 64:
-      e = a.causal ? launch_bwd_t<64, true>(a, p, s) : launch_bwd_t<64, false>(a, p, s);
-      break;
+  switch (a.d * 2 + (a.bf16 ? 1 : 0)) {
     case 128:
-      e = a.causal ? launch_bwd_t<128, true>(a, p, s) : launch_bwd_t<128, false>(a, p, s);
+      e = a.causal ? launch_bwd_t<64, true, _Float16>(a, p, s) : launch_bwd_t<64, false, _Float16>(a, p, s);
+      break;
+    case 129:
+      e = a.causal ? launch_bwd_t<64, true, __bf16>(a, p, s) : launch_bwd_t<64, false, __bf16>(a, p, s);
       break;
     case 256:
-      e = a.causal ? launch_bwd_t<256, true>(a, p, s) : launch_bwd_t<256, false>(a, p, s);
+      e = a.causal ? launch_bwd_t<128, true, _Float16>(a, p, s) : launch_bwd_t<128, false, _Float16>(a, p, s);
+      break;
+    case 257:
+      e = a.causal ? launch_bwd_t<128, true, __bf16>(a, p, s) : launch_bwd_t<128, false, __bf16>(a, p, s);
+      break;
+    case 512:
+      e = a.causal ? launch_bwd_t<256, true, _Float16>(a, p, s) : launch_bwd_t<256, false, _Float16>(a, p, s);
+      break;
+    case 513:
+      e = a.causal ? launch_bwd_t<256, true, __bf16>(a, p, s) : launch_bwd_t<256, false, __bf16>(a, p, s);
       break;
     default:
       e = hipErrorInvalidValue;

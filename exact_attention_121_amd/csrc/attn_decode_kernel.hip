@@ -39,7 +39,7 @@ struct DecParams {
   uint32_t q_sign, q_keep;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T>
 __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_decode_split_kernel(DecParams p) {
   using C = Cfg<D>;
   static_assert(C::QB == 1 && C::BM == kDecodeRows, "decode packs 128 rows per workgroup, 32 per wave");
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_decode_split
   STile<D> sa, sb;
   if (w.nt_w > t0) {
     const int kv0 = t0 * C::BN;
-    qk_tile<D>(k_stage<D>(smem, 0), w.qf, w.off, sa);
+    qk_tile<D, T>(k_stage<D>(smem, 0), w.qf, w.off, sa);
     if (kv0 + C::BN > Nk || (CAUSAL && kv0 + C::BN - 1 > w.qw0)) mask_tile<D, CAUSAL>(sa, kv0, Nk, w.qrow, w.g);
     tile_max<D>(sa, w.c, w.m_run);
     // A row that sees no key of this chunk (causal: the chunk starts after
@@ -117,8 +117,8 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_decode_split
   __syncthreads();
 
   for (int j = t0; j < t1; j += 2) {
-    pipeline_step<D, CAUSAL, 0>(j, t1, smem, krs, vrs, lo, tid, w, sa, sb);
-    if (j + 1 < t1) pipeline_step<D, CAUSAL, 1>(j + 1, t1, smem, krs, vrs, lo, tid, w, sb, sa);
+    pipeline_step<D, CAUSAL, 0, T>(j, t1, smem, krs, vrs, lo, tid, w, sa, sb);
+    if (j + 1 < t1) pipeline_step<D, CAUSAL, 1, T>(j + 1, t1, smem, krs, vrs, lo, tid, w, sb, sa);
   }
 
   // Partial result of this chunk for the rows that exist: O_s = O^T / l_s
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_decode_split
       for (int rq = 0; rq < 4; ++rq) {
         half4 h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = static_cast<_Float16>(w.oacc[0][dt][4 * rq + i] * inv1);
+        for (int i = 0; i < 4; ++i) h[i] = to_elem<T>(w.oacc[0][dt][4 * rq + i] * inv1);
         *reinterpret_cast<half4*>(out + 32 * dt + 8 * rq + 4 * w.g) = h;
       }
     if (p.lse != nullptr && w.g == 0)
@@ -181,7 +181,7 @@ constexpr int kMergeFewSplits = 64;
 // rule (m = max LSE_s, l = sum 2^(LSE_s - m), acc = sum 2^(LSE_s - m) O_s),
 // reading each split's LSE and O slice in the same pass; the threads then
 // combine theirs: LSE = m + log2 l, O = acc / l, rounded once to fp16.
-template <int D, int DS>
+template <int D, int DS, typename T>
 __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(MergeParams p) {
   constexpr int CH = DS / 4;                 // float4 chunks of a slice
   constexpr int PAR = kMergeThreads / CH;    // splits read at once
@@ -254,27 +254,27 @@ __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(MergeP
     }
     const float inv = 1.0f / L;
     half4 h;
-    h[0] = static_cast<_Float16>(o.x * inv);
-    h[1] = static_cast<_Float16>(o.y * inv);
-    h[2] = static_cast<_Float16>(o.z * inv);
-    h[3] = static_cast<_Float16>(o.w * inv);
+    h[0] = to_elem<T>(o.x * inv);
+    h[1] = to_elem<T>(o.y * inv);
+    h[2] = to_elem<T>(o.z * inv);
+    h[3] = to_elem<T>(o.w * inv);
     *reinterpret_cast<half4*>(p.o + (size_t)rowid * D + slice * DS + 4 * tid) = h;
     if (p.lse != nullptr && slice == 0 && tid == 0) p.lse[rowid] = (M + __builtin_log2f(L)) * kLn2;
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename T>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecParams& dp, const MergeParams& mp, hipStream_t s) {
   const unsigned groups = static_cast<unsigned>(a.B) * a.Hkv * static_cast<unsigned>(a.plan.row_blocks);
-  hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL>), dim3(groups * static_cast<unsigned>(a.plan.splits)),
+  hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL, T>), dim3(groups * static_cast<unsigned>(a.plan.splits)),
                      dim3(kThreads), 0, s, dp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.splits == 1) return e;
   const unsigned rows = static_cast<unsigned>(a.B) * a.Hq * a.Nq;
   if (a.plan.splits <= kMergeFewSplits)
-    hipLaunchKernelGGL((attn_decode_merge_kernel<D, D>), dim3(rows), dim3(kMergeThreads), 0, s, mp);
+    hipLaunchKernelGGL((attn_decode_merge_kernel<D, D, T>), dim3(rows), dim3(kMergeThreads), 0, s, mp);
   else
-    hipLaunchKernelGGL((attn_decode_merge_kernel<D, kMergeSliceDims>), dim3(rows * (D / kMergeSliceDims)),
+    hipLaunchKernelGGL((attn_decode_merge_kernel<D, kMergeSliceDims, T>), dim3(rows * (D / kMergeSliceDims)),
                        dim3(kMergeThreads), 0, s, mp);
   return hipGetLastError();
 }
@@ -317,15 +317,26 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   mp.splits = dp.splits;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  switch (a.d) {
-    case 64:
-      e = a.causal ? launch_decode_t<64, true>(a, dp, mp, s) : launch_decode_t<64, false>(a, dp, mp, s);
-      break;
+  switch (a.d * 2 + (a.bf16 ? 1 : 0)) {
     case 128:
-      e = a.causal ? launch_decode_t<128, true>(a, dp, mp, s) : launch_decode_t<128, false>(a, dp, mp, s);
+      e = a.causal ? launch_decode_t<64, true, _Float16>(a, dp, mp, s) : launch_decode_t<64, false, _Float16>(a, dp, mp, s);
+      break;
+    case 129:
+      e = a.causal ? launch_decode_t<64, true, __bf16>(a, dp, mp, s) : launch_decode_t<64, false, __bf16>(a, dp, mp, s);
       break;
     case 256:
-      e = a.causal ? launch_decode_t<256, true>(a, dp, mp, s) : launch_decode_t<256, false>(a, dp, mp, s);
+      e = a.causal ? launch_decode_t<128, true, _Float16>(a, dp, mp, s)
+                   : launch_decode_t<128, false, _Float16>(a, dp, mp, s);
+      break;
+    case 257:
+      e = a.causal ? launch_decode_t<128, true, __bf16>(a, dp, mp, s) : launch_decode_t<128, false, __bf16>(a, dp, mp, s);
+      break;
+    case 512:
+      e = a.causal ? launch_decode_t<256, true, _Float16>(a, dp, mp, s)
+                   : launch_decode_t<256, false, _Float16>(a, dp, mp, s);
+      break;
+    case 513:
+      e = a.causal ? launch_decode_t<256, true, __bf16>(a, dp, mp, s) : launch_decode_t<256, false, __bf16>(a, dp, mp, s);
       break;
     default:
       e = hipErrorInvalidValue;

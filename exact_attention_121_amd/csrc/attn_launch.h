@@ -73,6 +73,7 @@ struct DecodeArgs {
   int B, Hq, Hkv, Nq, Nk, d;
   float scale;
   int causal;
+  int bf16;    // element type of q, k, v, o: 0 = fp16, 1 = bf16
   DecodePlan plan;
 };
 
@@ -102,6 +103,7 @@ struct BwdArgs {
   int B, Hq, Hkv, N, d;
   float scale;
   int causal;
+  int bf16;    // element type of q, k, v, o, dout and the gradients: 0 = fp16, 1 = bf16
 };
 
 // Queues the three backward kernels (prep, dK/dV, dQ) on `stream`.

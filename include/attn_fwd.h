@@ -153,6 +153,15 @@ int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t workspace_bytes, struct ihipStream_t* stream);
 
 /*
+ * attn_decode_bf16 - attn_decode for bfloat16 q, k, v and o (same arguments,
+ * workspace, limits and status codes; lse and the workspace stay fp32).
+ */
+int attn_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                     int64_t d, float scale, int causal, void* workspace,
+                     int64_t workspace_bytes, struct ihipStream_t* stream);
+
+/*
  * attn_decode_workspace_size - bytes of workspace attn_decode needs for this
  * shape (0 for an empty problem), written to *bytes.  Host only.  Returns
  * ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED for shapes attn_decode would
@@ -207,6 +216,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
              float scale, int causal, void* workspace, int64_t workspace_bytes,
              struct ihipStream_t* stream);
+
+/*
+ * attn_bwd_bf16 - attn_bwd for bfloat16 q, k, v, o, dout and gradients (the
+ * output of attn_fwd_bf16); same arguments, workspace, limits and status
+ * codes.  P and dS are rounded to bf16 for the products that use them.
+ */
+int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, void* dq, void* dk,
+                  void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                  int64_t d, float scale, int causal, void* workspace,
+                  int64_t workspace_bytes, struct ihipStream_t* stream);
 
 /*
  * attn_bwd_workspace_size - bytes of workspace attn_bwd needs (0 for an
