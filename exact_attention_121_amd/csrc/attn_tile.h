@@ -59,12 +59,43 @@ constexpr int query_blocks() {
   return D == 64 ? ATTN_QB64 : (D == 128 ? ATTN_QB128 : ATTN_QB256);
 }
 
+// Keys per K/V tile and matrix operands read ahead of their MFMA, per
+// head_dim: the defaults are the measured best on gfx950; the offline tile
+// sweep (exact_attention_121_amd/tile_sweep.py) rebuilds the forward kernel
+// with other values.
+#ifndef ATTN_BN64
+#define ATTN_BN64 64
+#endif
+#ifndef ATTN_BN128
+#define ATTN_BN128 64
+#endif
+#ifndef ATTN_BN256
+#define ATTN_BN256 32
+#endif
+#ifndef ATTN_KAHEAD64
+#define ATTN_KAHEAD64 4
+#endif
+#ifndef ATTN_KAHEAD128
+#define ATTN_KAHEAD128 4
+#endif
+#ifndef ATTN_KAHEAD256
+#define ATTN_KAHEAD256 6
+#endif
+template <int D>
+constexpr int key_tile() {
+  return D == 64 ? ATTN_BN64 : (D == 128 ? ATTN_BN128 : ATTN_BN256);
+}
+template <int D>
+constexpr int k_ahead() {
+  return D == 64 ? ATTN_KAHEAD64 : (D == 128 ? ATTN_KAHEAD128 : ATTN_KAHEAD256);
+}
+
 template <int D>
 struct Cfg {
   static constexpr int QB = query_blocks<D>();     // 32-row query blocks per wave
   static constexpr int WAVE_ROWS = 32 * QB;        // query rows per wave
   static constexpr int BM = kWaves * WAVE_ROWS;    // query rows per workgroup
-  static constexpr int BN = (D == 256) ? 32 : 64;  // keys per K/V tile
+  static constexpr int BN = key_tile<D>();         // keys per K/V tile
   static constexpr int NT = BN / 32;               // 32-key sub-tiles of S^T
   static constexpr int DC = D / 16;                // 16-dim k-steps of Q.K
   static constexpr int DT = D / 32;                // 32-dim row tiles of O^T
@@ -74,8 +105,8 @@ struct Cfg {
   // Workgroups per CU the register budget allows.
   static constexpr int WG_PER_CU = (QB == 1 && D != 256) ? 2 : 1;
   // Matrix operands read from LDS ahead of their MFMA (K reads; twice as
-  // many V transpose reads, two per MFMA); measured on gfx950.
-  static constexpr int K_AHEAD = D == 256 ? 6 : 4;
+  // many V transpose reads, two per MFMA).
+  static constexpr int K_AHEAD = k_ahead<D>();
   static_assert(BN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
 };
 

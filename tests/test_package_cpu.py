@@ -1,0 +1,35 @@
+"""Package-level checks on the CPU: the product path never reaches the
+oracle, and the offline tile sweep's variant table is well formed."""
+
+import ast
+import os
+
+import exact_attention_121_amd as ea
+
+PKG = os.path.dirname(os.path.abspath(ea.__file__))
+
+
+def test_package_never_imports_the_oracle():
+    for name in sorted(os.listdir(PKG)):
+        if not name.endswith(".py"):
+            continue
+        tree = ast.parse(open(os.path.join(PKG, name)).read())
+        for node in ast.walk(tree):
+            mods = []
+            if isinstance(node, ast.Import):
+                mods = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                mods = [node.module or ""]
+            for m in mods:
+                assert not m.split(".")[0] == "oracle", f"{name} imports {m}"
+
+
+def test_tile_sweep_table():
+    from exact_attention_121_amd import tile_sweep as ts
+    for d, variants in ts.VARIANTS.items():
+        assert ts.DEFAULT[d] in variants, f"default of d={d} is not swept"
+        names = [ts.variant_name(d, v) for v in variants]
+        assert len(set(names)) == len(names)
+        for v in variants:
+            assert v["BN"] * (d // 8) % 256 == 0, "a tile must split evenly over 256 threads"
+    assert {c[0] for c in ts.CASES} <= set(ts.VARIANTS)
