@@ -24,6 +24,9 @@ per-chunk kernel and the merge kernel) on a named decode workload; the line
 reports HBM GB/s against the 8 TB/s peak.  When one copy of the cache is
 smaller than 1 GiB, the steps cycle over enough copies to exceed the chip's
 256 MB last-level cache, so that every step reads HBM.
+
+--head-dim D runs any of these on the chosen workload with head_dim D instead
+of its own (same seeds and other sizes, scale 1/sqrt(D)).
 """
 
 from __future__ import annotations
@@ -81,6 +84,15 @@ def measured_traffic(workload_name: str, path=TRAFFIC_FILE, sources=FORWARD_SOUR
     if not entry or entry.get("kernel_code_sha256_16") != kernel_source_hash(sources):
         return None
     return entry.get(key)
+
+
+def with_head_dim(w, d: int):
+    """The workload w with head_dim d instead of its own (0: unchanged), named
+    `<name>_d<d>`; the same seeds and every other size."""
+    if not d or d == w.d:
+        return w
+    import dataclasses
+    return dataclasses.replace(w, d=d, name=f"{w.name}_d{d}")
 
 
 def cpu_threads() -> int:
@@ -193,7 +205,7 @@ def run_decode(args) -> int:
     import exact_attention_121_amd as ea
     from exact_attention_121_amd.inputs import DECODE_WORKLOADS, make_decode_inputs
 
-    w = DECODE_WORKLOADS[args.decode]
+    w = with_head_dim(DECODE_WORKLOADS[args.decode], args.head_dim)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ea.load_library()
@@ -320,7 +332,7 @@ def run_backward(args) -> int:
     import exact_attention_121_amd as ea
     from exact_attention_121_amd.inputs import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
+    w = with_head_dim(WORKLOADS[args.workload], args.head_dim)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ea.load_library()
@@ -414,6 +426,9 @@ def main() -> int:
                          "bfloat16)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dQ, dK, dV) on --workload instead")
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="run the chosen workload with this head_dim instead of its own (a multiple of 32 "
+                         "from 32 to 256; scale 1/sqrt(head_dim))")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain elementwise copy of this many MiB (fp16 -> fp16, "
                          "y = -x) three times, so that hardware byte counters can be "
@@ -436,7 +451,7 @@ def main() -> int:
     import exact_attention_121_amd as ea
     from exact_attention_121_amd.inputs import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
+    w = with_head_dim(WORKLOADS[args.workload], args.head_dim)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ea.load_library()

@@ -32,4 +32,4 @@ from .binding import (  # noqa: F401
     load_library,
 )
 
-__version__ = "0.3.1"
+__version__ = "0.4.0"

@@ -37,7 +37,7 @@ class AttnError(RuntimeError):
 
 
 class AttnUnsupportedError(AttnError, NotImplementedError):
-    """head_dim outside {64, 128, 256}; the caller may use an unfused path."""
+    """head_dim not a multiple of 32 in [32, 256]; the caller may use an unfused path."""
 
 
 class AttnArgumentError(AttnError, ValueError):

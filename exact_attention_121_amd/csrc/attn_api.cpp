@@ -32,6 +32,10 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 // and the LSE as 4-byte words.
 bool misaligned(const void* p, uintptr_t align) { return (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0; }
 
+// Head dims the kernels are built for: the multiples of 32 from 32 to 256
+// (32-dim output tiles of the matrix instructions).
+bool head_dim_supported(int64_t d) { return d >= 32 && d <= 256 && d % 32 == 0; }
+
 bool misaligned_tensors(const void* q, const void* k, const void* v, const void* o, const float* lse) {
   return misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4);
 }
@@ -44,7 +48,7 @@ extern "C" int attn_check_args(const void* q, const void* k, const void* v, cons
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!head_dim_supported(d)) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || N == 0) return ATTN_OK;  // empty problem: nothing to touch
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_INVALID_ARG;
   if (misaligned_tensors(q, k, v, o, lse)) return ATTN_ERR_INVALID_ARG;
@@ -115,7 +119,7 @@ int check_decode_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t N
   if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!head_dim_supported(d)) return ATTN_ERR_UNSUPPORTED;
   if (Nq > Nk) return ATTN_ERR_INVALID_ARG;  // the queries are the last Nq of Nk positions
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (Nk > kLimitHead / d) return ATTN_ERR_INVALID_ARG;
@@ -211,7 +215,7 @@ extern "C" int attn_decode_bf16(const void* q, const void* k, const void* v, voi
 
 extern "C" int attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t N, int64_t d, int64_t* bytes) {
   if (bytes == nullptr || B < 0 || N < 0 || Hq < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!head_dim_supported(d)) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || N == 0) {
     *bytes = 0;
     return ATTN_OK;
@@ -228,7 +232,7 @@ extern "C" int attn_check_bwd_args(const void* q, const void* k, const void* v, 
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!head_dim_supported(d)) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || N == 0) return ATTN_OK;  // empty problem: nothing to touch
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
       dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
@@ -318,7 +322,7 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_INVALID_ARG:
       return "invalid argument (null pointer, size, head grouping, scale, overlap or limit)";
     case ATTN_ERR_UNSUPPORTED:
-      return "unsupported head_dim (must be 64, 128 or 256)";
+      return "unsupported head_dim (must be a multiple of 32 from 32 to 256)";
     case ATTN_ERR_DEVICE:
       return "the HIP runtime refused the kernel launch";
     default:
@@ -326,4 +330,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" const char* attn_version(void) { return "attn_fwd 0.3.1 gfx950"; }
+extern "C" const char* attn_version(void) { return "attn_fwd 0.4.0 gfx950"; }

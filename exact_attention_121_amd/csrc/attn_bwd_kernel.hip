@@ -71,12 +71,16 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------------------
-// Delta and LSE in log2 units.  D / 8 lanes per row (16-byte loads), the
-// row's partial dot products summed with lane shuffles.
+// Delta and LSE in log2 units.  A power-of-two group of lanes per row, D / 8
+// of them with a 16-byte load each, the row's partial dot products summed
+// with lane shuffles.
 // ---------------------------------------------------------------------------
+template <int D>
+constexpr int prep_lanes() { return D <= 32 ? 4 : (D <= 64 ? 8 : (D <= 128 ? 16 : 32)); }
+
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(BwdParams p) {
-  constexpr int CH = D / 8;                 // lanes per row
+  constexpr int CH = prep_lanes<D>();       // lanes per row
   constexpr int ROWS = kThreads / CH;       // rows per workgroup
   const int tid = threadIdx.x;
   const int row = blockIdx.x * ROWS + tid / CH;   // (b * Hq + hq) * Npad + i
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(BwdParams p) {
   const int bh = row / p.Npad;
   const int i = row - bh * p.Npad;
   float acc = 0.f;
-  if (i < p.N) {
+  if (i < p.N && part < D / 8) {
     const size_t off = ((size_t)bh * p.N + i) * D + part * 8;
     const half8 a = *reinterpret_cast<const half8*>(p.o + off);
     const half8 g = *reinterpret_cast<const half8*>(p.dout + off);
@@ -137,7 +141,11 @@ constexpr int bwd_dim_parts() { return D == 256 ? 2 : 1; }
 // dK/dV workgroups per CU the register budget allows (K, V and the two
 // accumulators stay in registers).
 template <int D>
-constexpr int bwd_dkdv_wg_per_cu() { return D == 64 ? 2 : 1; }
+constexpr int bwd_dkdv_wg_per_cu() { return D <= 64 ? 2 : 1; }
+
+// dQ workgroups per CU (Q, dO and the dQ accumulators stay in registers).
+template <int D>
+constexpr int bwd_dq_wg_per_cu() { return D <= 128 ? 2 : 1; }
 
 // pv_tile over NDT of the 32-dim output tiles, whose transpose-read lane
 // offsets are in voff (the dims of those tiles only).
@@ -312,8 +320,8 @@ __global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dk
     wait_vm_all();
     __syncthreads();
     };
-  if constexpr (D == 64) {
-    // Unrolled, this head_dim no longer fits two workgroups per CU.
+  if constexpr (D <= 64) {
+    // Unrolled, these head_dims no longer fit two workgroups per CU.
     for (int u = 0; u < steps; ++u) step(u & 1, u);
   } else {
     for (int u = 0; u < steps; u += 2) {
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dk
 // the lanes' columns), K and V tiles stream through LDS.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, typename T>
-__global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_bwd_dq_kernel(BwdParams p, int q_tiles) {
+__global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_kernel(BwdParams p, int q_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-row block per wave");
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
@@ -463,7 +471,7 @@ __global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_bwd_dq_kerne
 template <int D, bool CAUSAL, typename T>
 hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   using C = Cfg<D>;
-  constexpr int rows_per_wg = kThreads / (D / 8);
+  constexpr int rows_per_wg = kThreads / prep_lanes<D>();
   const unsigned prep_grid = static_cast<unsigned>((p.rows_total + rows_per_wg - 1) / rows_per_wg);
   hipLaunchKernelGGL((attn_bwd_prep_kernel<D, T>), dim3(prep_grid), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
@@ -504,29 +512,12 @@ int launch_backward(const BwdArgs& a, void* stream) {
   p.c = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);
   p.scale = a.scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (a.d * 2 + (a.bf16 ? 1 : 0)) {
-    case 128:
-      e = a.causal ? launch_bwd_t<64, true, _Float16>(a, p, s) : launch_bwd_t<64, false, _Float16>(a, p, s);
-      break;
-    case 129:
-      e = a.causal ? launch_bwd_t<64, true, __bf16>(a, p, s) : launch_bwd_t<64, false, __bf16>(a, p, s);
-      break;
-    case 256:
-      e = a.causal ? launch_bwd_t<128, true, _Float16>(a, p, s) : launch_bwd_t<128, false, _Float16>(a, p, s);
-      break;
-    case 257:
-      e = a.causal ? launch_bwd_t<128, true, __bf16>(a, p, s) : launch_bwd_t<128, false, __bf16>(a, p, s);
-      break;
-    case 512:
-      e = a.causal ? launch_bwd_t<256, true, _Float16>(a, p, s) : launch_bwd_t<256, false, _Float16>(a, p, s);
-      break;
-    case 513:
-      e = a.causal ? launch_bwd_t<256, true, __bf16>(a, p, s) : launch_bwd_t<256, false, __bf16>(a, p, s);
-      break;
-    default:
-      e = hipErrorInvalidValue;
-  }
+  const hipError_t e = with_head_dim(a.d, [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    if (a.bf16)
+      return a.causal ? launch_bwd_t<D, true, __bf16>(a, p, s) : launch_bwd_t<D, false, __bf16>(a, p, s);
+    return a.causal ? launch_bwd_t<D, true, _Float16>(a, p, s) : launch_bwd_t<D, false, _Float16>(a, p, s);
+  });
   return static_cast<int>(e);
 }
 

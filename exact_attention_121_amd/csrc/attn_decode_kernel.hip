@@ -186,6 +186,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(MergeP
   constexpr int CH = DS / 4;                 // float4 chunks of a slice
   constexpr int PAR = kMergeThreads / CH;    // splits read at once
   constexpr int SLICES = D / DS;
+  static_assert(kMergeThreads % CH == 0 && D % DS == 0, "the splits must cover the workgroup evenly");
   __shared__ float sm_m[PAR][CH], sm_l[PAR][CH];
   __shared__ float4 sm_acc[PAR][CH];
 
@@ -265,14 +266,20 @@ __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(MergeP
 
 template <int D, bool CAUSAL, typename T>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecParams& dp, const MergeParams& mp, hipStream_t s) {
+  static_assert(Cfg<D>::BN == decode_key_tile(D), "the decode plan and the kernel must use the same key tile");
+  static_assert(Cfg<D>::WG_PER_CU * 256 == decode_target_groups(D), "the split plan must fill the chip once");
   const unsigned groups = static_cast<unsigned>(a.B) * a.Hkv * static_cast<unsigned>(a.plan.row_blocks);
   hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL, T>), dim3(groups * static_cast<unsigned>(a.plan.splits)),
                      dim3(kThreads), 0, s, dp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.splits == 1) return e;
   const unsigned rows = static_cast<unsigned>(a.B) * a.Hq * a.Nq;
-  if (a.plan.splits <= kMergeFewSplits)
-    hipLaunchKernelGGL((attn_decode_merge_kernel<D, D, T>), dim3(rows), dim3(kMergeThreads), 0, s, mp);
+  // Whole rows need kMergeThreads to split evenly into D / 4 lanes per split
+  // (head_dims 32, 64, 128, 256); other head_dims always take 32-dim slices.
+  constexpr bool kWholeRows = kMergeThreads % (D / 4) == 0;
+  if (kWholeRows && a.plan.splits <= kMergeFewSplits)
+    hipLaunchKernelGGL((attn_decode_merge_kernel<D, kWholeRows ? D : kMergeSliceDims, T>), dim3(rows),
+                       dim3(kMergeThreads), 0, s, mp);
   else
     hipLaunchKernelGGL((attn_decode_merge_kernel<D, kMergeSliceDims, T>), dim3(rows * (D / kMergeSliceDims)),
                        dim3(kMergeThreads), 0, s, mp);
@@ -316,31 +323,13 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   mp.row_blocks = dp.row_blocks;
   mp.splits = dp.splits;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (a.d * 2 + (a.bf16 ? 1 : 0)) {
-    case 128:
-      e = a.causal ? launch_decode_t<64, true, _Float16>(a, dp, mp, s) : launch_decode_t<64, false, _Float16>(a, dp, mp, s);
-      break;
-    case 129:
-      e = a.causal ? launch_decode_t<64, true, __bf16>(a, dp, mp, s) : launch_decode_t<64, false, __bf16>(a, dp, mp, s);
-      break;
-    case 256:
-      e = a.causal ? launch_decode_t<128, true, _Float16>(a, dp, mp, s)
-                   : launch_decode_t<128, false, _Float16>(a, dp, mp, s);
-      break;
-    case 257:
-      e = a.causal ? launch_decode_t<128, true, __bf16>(a, dp, mp, s) : launch_decode_t<128, false, __bf16>(a, dp, mp, s);
-      break;
-    case 512:
-      e = a.causal ? launch_decode_t<256, true, _Float16>(a, dp, mp, s)
-                   : launch_decode_t<256, false, _Float16>(a, dp, mp, s);
-      break;
-    case 513:
-      e = a.causal ? launch_decode_t<256, true, __bf16>(a, dp, mp, s) : launch_decode_t<256, false, __bf16>(a, dp, mp, s);
-      break;
-    default:
-      e = hipErrorInvalidValue;
-  }
+  const hipError_t e = with_head_dim(a.d, [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    if (a.bf16)
+      return a.causal ? launch_decode_t<D, true, __bf16>(a, dp, mp, s) : launch_decode_t<D, false, __bf16>(a, dp, mp, s);
+    return a.causal ? launch_decode_t<D, true, _Float16>(a, dp, mp, s)
+                    : launch_decode_t<D, false, _Float16>(a, dp, mp, s);
+  });
   return static_cast<int>(e);
 }
 

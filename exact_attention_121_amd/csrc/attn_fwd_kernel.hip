@@ -229,20 +229,10 @@ int launch_forward(const LaunchArgs& a, void* stream) {
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
   p.q_keep = a.scale == 0.f ? 0u : 0xffffffffu;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (a.d) {
-    case 64:
-      e = a.causal ? launch_t<64, true>(a, p, s) : launch_t<64, false>(a, p, s);
-      break;
-    case 128:
-      e = a.causal ? launch_t<128, true>(a, p, s) : launch_t<128, false>(a, p, s);
-      break;
-    case 256:
-      e = a.causal ? launch_t<256, true>(a, p, s) : launch_t<256, false>(a, p, s);
-      break;
-    default:
-      e = hipErrorInvalidValue;
-  }
+  const hipError_t e = with_head_dim(a.d, [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    return a.causal ? launch_t<D, true>(a, p, s) : launch_t<D, false>(a, p, s);
+  });
   return static_cast<int>(e);
 }
 

@@ -8,7 +8,8 @@
 namespace attn {
 
 // Arguments after validation: every size fits the kernel's 32-bit index math
-// (N * d <= 2^30, B * Hq * ceil(N / 128) < 2^31) and d is 64, 128 or 256.
+// (N * d <= 2^30, B * Hq * ceil(N / 128) < 2^31) and d is a multiple of 32
+// from 32 to 256.
 struct LaunchArgs {
   const void* q;
   const void* k;
@@ -35,16 +36,27 @@ int launch_forward(const LaunchArgs& a, void* stream);
 // the launcher so both see the same plan.
 constexpr int64_t kDecodeRows = 128;  // packed rows per workgroup
 
-// Workgroups the chip holds at once (256 CUs; two per CU with head_dim 64 or
-// 128, one with 256): the split count aims at one full round of them.
-inline int64_t decode_target_groups(int64_t d) { return d == 256 ? 256 : 512; }
+// Workgroups per CU of the forward and decode kernels' default build: two
+// (each SIMD interleaves two waves) wherever the registers of a 32-row query
+// block hold Q, the output accumulators and two score tiles without
+// spilling, i.e. up to d = 224; one at d = 256.
+constexpr int64_t default_wg_per_cu(int64_t d) { return d <= 224 ? 2 : 1; }
+
+// Workgroups the chip holds at once (256 CUs times the workgroups per CU):
+// the split count aims at one full round of them.
+constexpr int64_t decode_target_groups(int64_t d) { return 256 * default_wg_per_cu(d); }
 
 struct DecodePlan {
   int64_t row_blocks, kv_tiles, splits, chunk_tiles;
   int64_t workspace_bytes;  // partial O (fp32) and LSE (fp32) of every split
 };
 
-inline int64_t decode_key_tile(int64_t d) { return d == 256 ? 32 : 64; }
+// Keys per K/V tile of the kernels' default build, per head_dim: 64 up to
+// d = 128 (two workgroups per CU), 32 above (one workgroup per CU; the
+// output accumulators take the other half of the register file).
+constexpr int64_t default_key_tile(int64_t d) { return d > 128 ? 32 : 64; }
+
+constexpr int64_t decode_key_tile(int64_t d) { return default_key_tile(d); }
 
 inline DecodePlan decode_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d) {
   DecodePlan p;

@@ -56,38 +56,82 @@ constexpr int kBufferWord3 = 0x00020000;
 #endif
 template <int D>
 constexpr int query_blocks() {
-  return D == 64 ? ATTN_QB64 : (D == 128 ? ATTN_QB128 : ATTN_QB256);
+  return D == 64 ? ATTN_QB64 : (D == 128 ? ATTN_QB128 : (D == 256 ? ATTN_QB256 : 1));
 }
 
 // Keys per K/V tile and matrix operands read ahead of their MFMA, per
-// head_dim: the defaults are the measured best on gfx950; the offline tile
-// sweep (exact_attention_121_amd/tile_sweep.py) rebuilds the forward kernel
-// with other values.
+// head_dim.  The defaults (default_key_tile in attn_launch.h, k_ahead below)
+// are the measured best on gfx950; the offline tile sweep
+// (exact_attention_121_amd/tile_sweep.py) rebuilds the forward kernel with
+// other values through these hooks (0 = the default).
+#ifndef ATTN_BN32
+#define ATTN_BN32 0
+#endif
 #ifndef ATTN_BN64
-#define ATTN_BN64 64
+#define ATTN_BN64 0
+#endif
+#ifndef ATTN_BN96
+#define ATTN_BN96 0
 #endif
 #ifndef ATTN_BN128
-#define ATTN_BN128 64
+#define ATTN_BN128 0
+#endif
+#ifndef ATTN_BN160
+#define ATTN_BN160 0
+#endif
+#ifndef ATTN_BN192
+#define ATTN_BN192 0
+#endif
+#ifndef ATTN_BN224
+#define ATTN_BN224 0
 #endif
 #ifndef ATTN_BN256
-#define ATTN_BN256 32
+#define ATTN_BN256 0
+#endif
+#ifndef ATTN_KAHEAD32
+#define ATTN_KAHEAD32 0
 #endif
 #ifndef ATTN_KAHEAD64
-#define ATTN_KAHEAD64 4
+#define ATTN_KAHEAD64 0
+#endif
+#ifndef ATTN_KAHEAD96
+#define ATTN_KAHEAD96 0
 #endif
 #ifndef ATTN_KAHEAD128
-#define ATTN_KAHEAD128 4
+#define ATTN_KAHEAD128 0
+#endif
+#ifndef ATTN_KAHEAD160
+#define ATTN_KAHEAD160 0
+#endif
+#ifndef ATTN_KAHEAD192
+#define ATTN_KAHEAD192 0
+#endif
+#ifndef ATTN_KAHEAD224
+#define ATTN_KAHEAD224 0
 #endif
 #ifndef ATTN_KAHEAD256
-#define ATTN_KAHEAD256 6
+#define ATTN_KAHEAD256 0
 #endif
 template <int D>
 constexpr int key_tile() {
-  return D == 64 ? ATTN_BN64 : (D == 128 ? ATTN_BN128 : ATTN_BN256);
+  constexpr int hook = D == 32 ? ATTN_BN32 : D == 64 ? ATTN_BN64 : D == 96 ? ATTN_BN96 : D == 128 ? ATTN_BN128
+                     : D == 160 ? ATTN_BN160 : D == 192 ? ATTN_BN192 : D == 224 ? ATTN_BN224 : ATTN_BN256;
+  return hook ? hook : static_cast<int>(default_key_tile(D));
 }
 template <int D>
 constexpr int k_ahead() {
-  return D == 64 ? ATTN_KAHEAD64 : (D == 128 ? ATTN_KAHEAD128 : ATTN_KAHEAD256);
+  constexpr int hook = D == 32 ? ATTN_KAHEAD32 : D == 64 ? ATTN_KAHEAD64 : D == 96 ? ATTN_KAHEAD96
+                     : D == 128 ? ATTN_KAHEAD128 : D == 160 ? ATTN_KAHEAD160 : D == 192 ? ATTN_KAHEAD192
+                     : D == 224 ? ATTN_KAHEAD224 : ATTN_KAHEAD256;
+  return hook ? hook : (D <= 128 ? 4 : 6);
+}
+
+// 16-byte chunks per row of an LDS tile: the row's D / 8 chunks, padded to
+// 8, 16 or 32 so that the XOR swizzle below permutes whole rows (head_dims
+// other than 64, 128 and 256 leave the padding slots unused).
+template <int D>
+constexpr int lds_row_chunks() {
+  return D <= 64 ? 8 : (D <= 128 ? 16 : 32);
 }
 
 template <int D>
@@ -99,11 +143,12 @@ struct Cfg {
   static constexpr int NT = BN / 32;               // 32-key sub-tiles of S^T
   static constexpr int DC = D / 16;                // 16-dim k-steps of Q.K
   static constexpr int DT = D / 32;                // 32-dim row tiles of O^T
-  static constexpr int CPR = D / 8;                // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BN * D * 2;    // one K (or V) tile
+  static constexpr int CPR = lds_row_chunks<D>();  // 16-byte chunks per LDS tile row
+  static constexpr int SRC_CPR = D / 8;            // 16-byte chunks per row in memory
+  static constexpr int TILE_BYTES = BN * CPR * 16;   // one K (or V) tile in LDS
   static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
   // Workgroups per CU the register budget allows.
-  static constexpr int WG_PER_CU = (QB == 1 && D != 256) ? 2 : 1;
+  static constexpr int WG_PER_CU = QB == 1 ? static_cast<int>(default_wg_per_cu(D)) : 1;
   // Matrix operands read from LDS ahead of their MFMA (K reads; twice as
   // many V transpose reads, two per MFMA).
   static constexpr int K_AHEAD = k_ahead<D>();
@@ -128,9 +173,17 @@ __device__ __forceinline__ int swz(int r, int c) {
   return (r * Cfg<D>::CPR + (c ^ f)) * 16;
 }
 
+// Source offset of an LDS padding slot: 2^31 past the tile base.  For a
+// real tile (base below 2^31) that lies outside the head, which is at most
+// 2^31 bytes, so the range check turns the copy into zeros; for a skipped
+// tile (below) the sum wraps to offset 0, an in-bounds read.  Either way the
+// slot is never read by a matrix operand.
+constexpr uint32_t kPadChunk = 0x80000000u;
+
 // Byte offsets, relative to a tile's first row, of the 16-byte chunks that
 // thread `tid` copies into a swizzled tile (the chunk that belongs at
-// position p % CPR of row p / CPR of the tile).
+// position p % CPR of row p / CPR of the tile, or kPadChunk for a padding
+// slot).
 template <int D>
 struct LoadOffsets {
   uint32_t src[Cfg<D>::LOADS];
@@ -141,7 +194,10 @@ struct LoadOffsets {
       const int p = i * kThreads + tid;  // destination chunk; lanes of a wave are consecutive
       const int row = p / C::CPR;
       const int chunk = (swz<D>(row, p % C::CPR) >> 4) - row * C::CPR;
-      src[i] = static_cast<uint32_t>((row * D + chunk * 8) * 2);
+      if constexpr (C::CPR == C::SRC_CPR)
+        src[i] = static_cast<uint32_t>((row * D + chunk * 8) * 2);
+      else
+        src[i] = chunk < C::SRC_CPR ? static_cast<uint32_t>((row * D + chunk * 8) * 2) : kPadChunk;
     }
   }
 };
@@ -191,25 +247,35 @@ __device__ __forceinline__ float xlane_sum(float x) {
 
 // Per-lane LDS byte offsets of the matrix operands inside a (swizzled) tile.
 // Tile rows 32*t + 16*h (K) or key groups (V) only add a constant, so every
-// operand read is one of these registers plus an immediate offset.
+// operand read is one of these registers plus an immediate offset.  In rows
+// of 32 chunks the swizzle changes only the low four bits of the chunk
+// index, so chunk c + 16 lies 256 bytes after chunk c: the upper half of the
+// dims reuses the lower half's registers with an immediate offset.
 template <int D>
 struct Offsets {
-  int k[Cfg<D>::DC];       // K rows lane%32 (+32 t), chunk 2 dc + lane/32
-  int v[2][Cfg<D>::DT];    // V keys 4 g + (lane%16)/4 (+8 for [1]), dims of row tile dt
+  using C = Cfg<D>;
+  static constexpr bool kHalves = C::CPR == 32;
+  static constexpr int KR = kHalves && C::DC > 8 ? 8 : C::DC;  // registers for K chunks
+  static constexpr int VR = kHalves && C::DT > 4 ? 4 : C::DT;  // registers for V row tiles
+  int k[KR];       // K rows lane%32 (+32 t), chunk 2 dc + lane/32
+  int v[2][VR];    // V keys 4 g + (lane%16)/4 (+8 for [1]), dims of row tile dt
   __device__ __forceinline__ void init(int lane) {
-    using C = Cfg<D>;
     const int lr = lane & 31, g = lane >> 5, m16 = lane & 15;
 #pragma unroll
-    for (int dc = 0; dc < C::DC; ++dc) k[dc] = swz<D>(lr, 2 * dc + g);
+    for (int dc = 0; dc < KR; ++dc) k[dc] = swz<D>(lr, 2 * dc + g);
     const int dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);  // dim offset inside a 32-dim tile
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
+      for (int dt = 0; dt < VR; ++dt) {
         const int dim = 32 * dt + dsub;
         v[hi][dt] = swz<D>(4 * g + (m16 >> 2) + 8 * hi, dim >> 3) + (dim & 7) * 2;
       }
   }
+  // Offset of K chunk pair dc and of V row tile dt (dc, dt compile-time in
+  // the unrolled loops, so the choice and the +256 fold away).
+  __device__ __forceinline__ int kofs(int dc) const { return dc < KR ? k[dc] : k[dc - 8] + 256; }
+  __device__ __forceinline__ int vofs(int hi, int dt) const { return dt < VR ? v[hi][dt] : v[hi][dt - 4] + 256; }
 };
 
 template <int D>
@@ -257,7 +323,7 @@ __device__ __forceinline__ void qk_tile(const char* ks, const QFrag<D>& qf, cons
   for (int dc = 0; dc < C::DC; ++dc)
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
-      const half8 a = *reinterpret_cast<const half8*>(ks + off.k[dc] + 32 * t * C::CPR * 16);
+      const half8 a = *reinterpret_cast<const half8*>(ks + off.kofs(dc) + 32 * t * C::CPR * 16);
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb)
         s[qb][t] = mfma16<T>(a, qf[qb][dc], s[qb][t]);
@@ -385,8 +451,8 @@ __device__ __forceinline__ void pv_tile(const char* vs, const PTile<D>& pf, cons
       const int kb = (32 * t + 16 * h) * C::CPR * 16;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const short4v lo = tr_read(vs + off.v[0][dt] + kb);
-        const short4v hi = tr_read(vs + off.v[1][dt] + kb);
+        const short4v lo = tr_read(vs + off.vofs(0, dt) + kb);
+        const short4v hi = tr_read(vs + off.vofs(1, dt) + kb);
         const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < C::QB; ++qb)
@@ -411,6 +477,23 @@ template <int D>
 __device__ __forceinline__ char* k_stage(char* smem, int st) { return smem + st * Cfg<D>::TILE_BYTES; }
 template <int D>
 __device__ __forceinline__ char* v_stage(char* smem, int st) { return smem + (2 + st) * Cfg<D>::TILE_BYTES; }
+
+// Calls f(std::integral_constant<int, D>{}) for a supported head_dim d
+// (a multiple of 32 from 32 to 256) and returns its status.
+template <typename F>
+__host__ hipError_t with_head_dim(int d, F&& f) {
+  switch (d) {
+    case 32: return f(std::integral_constant<int, 32>{});
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 96: return f(std::integral_constant<int, 96>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    case 160: return f(std::integral_constant<int, 160>{});
+    case 192: return f(std::integral_constant<int, 192>{});
+    case 224: return f(std::integral_constant<int, 224>{});
+    case 256: return f(std::integral_constant<int, 256>{});
+    default: return hipErrorInvalidValue;
+  }
+}
 
 // Instruction groups for the compiler's scheduler (masks of
 // __builtin_amdgcn_sched_group_barrier).

@@ -9,6 +9,7 @@ per (head_dim, causal) case.
 
     python -m exact_attention_121_amd.tile_sweep build    # compile the variants (no GPU needed)
     python -m exact_attention_121_amd.tile_sweep run      # check and time them on cuda:0
+    (--dims 96,160 restricts either step to those head_dims)
 
 Choices swept (the compile-time hooks of csrc/attn_tile.h, per head_dim):
 keys per K/V tile (ATTN_BN*) and matrix operands read ahead of their MFMA
@@ -40,15 +41,24 @@ from .build import ARCH, CSRC, LIB_DIR, LIB_PATH, _hipcc, hip_flags
 SWEEP_DIR = os.path.join(LIB_DIR, "sweep")  # beside the library, so that the variants reach the GPU host
 
 # (head_dim, causal, B, H, N): the head_dim/causal combinations of the named
-# workloads at sizes that time in milliseconds.
-CASES = [(64, True, 8, 16, 4096), (128, False, 2, 32, 2048), (128, True, 1, 32, 8192), (256, True, 1, 32, 8192)]
+# workloads at sizes that time in milliseconds, and the LLaMA-7B layer shape
+# (B=2, H=32, N=2048, non-causal) at the other head_dims.
+CASES = [(64, True, 8, 16, 4096), (128, False, 2, 32, 2048), (128, True, 1, 32, 8192), (256, True, 1, 32, 8192),
+         (32, False, 2, 32, 2048), (96, False, 2, 32, 2048), (160, False, 2, 32, 2048), (192, False, 2, 32, 2048),
+         (224, False, 2, 32, 2048)]
 
 VARIANTS = {
+    32: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4)],
     64: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
+    96: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
     128: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
+    160: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64) for ka in (4, 6, 8)],
+    192: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64) for ka in (4, 6, 8)],
+    224: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64) for ka in (4, 6, 8)],
     256: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64) for ka in (4, 6, 8)],
 }
-DEFAULT = {64: dict(BN=64, KAHEAD=4), 128: dict(BN=64, KAHEAD=4), 256: dict(BN=32, KAHEAD=6)}
+# The default build's choices (csrc/attn_launch.h default_key_tile, csrc/attn_tile.h k_ahead).
+DEFAULT = {d: dict(BN=64 if d <= 128 else 32, KAHEAD=4 if d <= 128 else 6) for d in VARIANTS}
 
 
 def variant_name(d: int, v: dict) -> str:
@@ -61,7 +71,7 @@ def _run(cmd):
         raise RuntimeError(f"{' '.join(cmd)}\n{res.stderr[-2000:]}")
 
 
-def build_variants(jobs: int = 8) -> list[str]:
+def build_variants(jobs: int = 8, dims=None) -> list[str]:
     """Compile the default decode/backward/API objects once and one forward
     object per variant; link one library per variant into lib/sweep/."""
     os.makedirs(SWEEP_DIR, exist_ok=True)
@@ -88,7 +98,7 @@ def build_variants(jobs: int = 8) -> list[str]:
         except RuntimeError as e:
             return name, f"build failed: {str(e).splitlines()[-1][:200]}"
 
-    items = [(d, v) for d in VARIANTS for v in VARIANTS[d]]
+    items = [(d, v) for d in VARIANTS if dims is None or d in dims for v in VARIANTS[d]]
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         out = list(ex.map(one, items))
     for name, status in out:
@@ -104,13 +114,15 @@ def _load(path):
     return lib
 
 
-def run_sweep(repeats: int = 5) -> None:
+def run_sweep(repeats: int = 5, dims=None) -> None:
     import torch
 
     dev = torch.device("cuda:0")
     default = _load(LIB_PATH)
     best = {}
     for d, causal, B, H, N in CASES:
+        if dims is not None and d not in dims:
+            continue
         g = torch.Generator(device=dev)
         g.manual_seed(1000 + d + N)
         q = torch.randn(B, H, N, d, device=dev, generator=g).half()
@@ -172,11 +184,13 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("what", choices=("build", "run"))
     ap.add_argument("--jobs", type=int, default=8)
+    ap.add_argument("--dims", default="", help="comma-separated head_dims (default: all)")
     args = ap.parse_args()
+    dims = {int(x) for x in args.dims.split(",")} if args.dims else None
     if args.what == "build":
-        build_variants(args.jobs)
+        build_variants(args.jobs, dims)
     else:
-        run_sweep()
+        run_sweep(dims=dims)
     return 0
 
 

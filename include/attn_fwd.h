@@ -30,9 +30,11 @@
  *     lse is [B][Hq][N] IEEE binary32.
  *   - GQA / MQA ([FA-Infer] section 6): Hq must be a multiple of Hkv; query
  *     head h reads key/value head h / (Hq / Hkv) (contiguous groups).
- *   - head_dim ([CANN-FA], the closing note on head_dim): d must be 64, 128
- *     or 256.  The pages fall back to unfused attention for other values;
- *     this library instead returns ATTN_ERR_UNSUPPORTED and launches nothing.
+ *   - head_dim ([CANN-FA], the closing note on head_dim): the pages' fused
+ *     operator takes d = 64, 128 or 256 and falls back to unfused attention
+ *     for other values.  This library runs the same fused kernels for every
+ *     multiple of 32 from 32 to 256 (32, 64, 96, 128, 160, 192, 224, 256);
+ *     for any other d it returns ATTN_ERR_UNSUPPORTED and launches nothing.
  *   - causal != 0: key j is visible to query i iff j <= i ([CANN-FA] section
  *     "Calling FlashAttention from PyTorch", is_causal).  Queries and keys
  *     have the same length N.
@@ -64,7 +66,7 @@ enum attn_status {
   ATTN_ERR_INVALID_ARG = 1, /* NULL or misaligned pointer, bad size, bad grouping,
                                non-finite scale, overlapping output, size over
                                limits, workspace too small */
-  ATTN_ERR_UNSUPPORTED = 2, /* head_dim not in {64, 128, 256} */
+  ATTN_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 32 in [32, 256] */
   ATTN_ERR_DEVICE = 3       /* the HIP runtime refused the launch */
 };
 
@@ -78,7 +80,7 @@ enum attn_status {
  *   B, N   >= 0; B == 0 or N == 0 is an empty problem: ATTN_OK, nothing is
  *          launched and no pointer is touched (they may then be NULL)
  *   Hq, Hkv >= 1 with Hq % Hkv == 0
- *   d      64, 128 or 256
+ *   d      a multiple of 32 from 32 to 256
  *   scale  finite multiplier on q.k (1/sqrt(d) in the pages' usage,
  *          [FA-Dict] sections "Fused kernel" and "Calling"); any finite
  *          value, including 0 and negative values, is accepted

@@ -63,7 +63,7 @@ def test_valid_arguments():
     assert check() == ea.ATTN_OK
     assert check(lse=None) == ea.ATTN_OK
     assert check(scale=0.0) == ea.ATTN_OK and check(scale=-0.5) == ea.ATTN_OK
-    for d in (64, 128, 256):
+    for d in (32, 64, 96, 128, 160, 192, 224, 256):
         assert check(d=d) == ea.ATTN_OK
     assert check(Hq=8, Hkv=8) == ea.ATTN_OK and check(Hq=8, Hkv=1) == ea.ATTN_OK
     assert check(q=P + 16, o=4 * P + 48, lse=5 * P + 4) == ea.ATTN_OK   # 16- and 4-byte alignment suffice
@@ -99,10 +99,11 @@ def test_invalid_arguments(over):
     assert check(**over) == ea.ATTN_ERR_INVALID_ARG, over
 
 
-@pytest.mark.parametrize("d", [1, 32, 80, 96, 100, 129, 192, 512])
+@pytest.mark.parametrize("d", [1, 8, 16, 48, 80, 100, 129, 240, 288, 320, 512])
 def test_unsupported_head_dims(d):
-    # The pages fall back to unfused attention for other head_dims; the library
-    # reports it instead, whatever the pointers.
+    # The pages fall back to unfused attention for head_dims their kernel does
+    # not take; this library takes every multiple of 32 up to 256 and reports
+    # anything else, whatever the pointers.
     assert check(d=d) == ea.ATTN_ERR_UNSUPPORTED
     assert check(d=d, q=None) == ea.ATTN_ERR_UNSUPPORTED
 
@@ -151,7 +152,7 @@ def _plan(B, Hq, Hkv, Nq, Nk, d):
     chunk; the workspace holds a partial O row and LSE per row slot."""
     rows = (Hq // Hkv) * Nq
     row_blocks = -(-rows // 128)
-    bn = 32 if d == 256 else 64
+    bn = 32 if d > 128 else 64
     kv_tiles = -(-Nk // bn)
     groups = B * Hkv * row_blocks
     s = max(1, min(kv_tiles, -(-(256 if d == 256 else 512) // groups)))
@@ -163,6 +164,8 @@ def _plan(B, Hq, Hkv, Nq, Nk, d):
 @pytest.mark.parametrize("shape", [
     (1, 1, 1, 1, 1, 64), (1, 32, 8, 1, 8192, 256), (1, 32, 1, 1, 131072, 128), (4, 32, 8, 16, 4096, 128),
     (2, 8, 2, 4, 1000, 64), (1, 64, 1, 16, 300, 128), (64, 32, 32, 1, 2048, 128),
+    (1, 8, 2, 1, 5000, 32), (2, 16, 4, 3, 777, 96), (1, 32, 8, 1, 8192, 160), (1, 12, 4, 2, 999, 192),
+    (3, 8, 1, 1, 4096, 224),
 ])
 def test_decode_workspace_size(shape):
     groups, splits, nbytes = _plan(*shape)
@@ -178,7 +181,7 @@ def test_decode_workspace_size_empty_and_invalid():
     with pytest.raises(ea.AttnError):
         ea.attn_decode_workspace_size(2, 8, 3, 1, 4, 128)        # Hq % Hkv != 0
     with pytest.raises(ea.AttnError):
-        ea.attn_decode_workspace_size(2, 8, 2, 1, 4, 96)         # head_dim
+        ea.attn_decode_workspace_size(2, 8, 2, 1, 4, 80)         # head_dim
     lib = ea.load_library()
     assert lib.attn_decode_workspace_size(1, 1, 1, 1, 1, 64, None) == ea.ATTN_ERR_INVALID_ARG
 
@@ -189,7 +192,7 @@ def test_decode_valid_arguments():
     assert dcheck(Nq=1000) == ea.ATTN_OK                          # Nq == Nk
     assert dcheck(Hkv=1) == ea.ATTN_OK and dcheck(Hkv=8) == ea.ATTN_OK
     assert dcheck(scale=0.0) == ea.ATTN_OK and dcheck(scale=-1.0) == ea.ATTN_OK
-    for d in (64, 128, 256):
+    for d in (32, 64, 96, 128, 160, 192, 224, 256):
         assert dcheck(d=d) == ea.ATTN_OK
     assert dcheck(workspace_bytes=1 << 40) == ea.ATTN_OK          # larger than needed is fine
     far = 1 << 44
@@ -228,7 +231,7 @@ def test_decode_short_workspace_is_rejected():
     assert dcheck(workspace_bytes=need - 1) == ea.ATTN_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("d", [32, 80, 96, 192])
+@pytest.mark.parametrize("d", [16, 48, 80, 200, 288])
 def test_decode_unsupported_head_dims(d):
     assert dcheck(d=d, workspace_bytes=1 << 30) == ea.ATTN_ERR_UNSUPPORTED
 
@@ -282,7 +285,7 @@ def test_bwd_workspace_size_empty_and_invalid():
     assert ea.attn_bwd_workspace_size(0, 8, 100, 128) == 0
     assert ea.attn_bwd_workspace_size(2, 8, 0, 128) == 0
     with pytest.raises(ea.AttnError):
-        ea.attn_bwd_workspace_size(2, 8, 100, 96)
+        ea.attn_bwd_workspace_size(2, 8, 100, 80)
     with pytest.raises(ea.AttnError):
         ea.attn_bwd_workspace_size(-1, 8, 100, 128)
     assert ea.load_library().attn_bwd_workspace_size(1, 1, 1, 64, None) == ea.ATTN_ERR_INVALID_ARG
@@ -291,7 +294,7 @@ def test_bwd_workspace_size_empty_and_invalid():
 def test_bwd_valid_arguments():
     assert bcheck() == ea.ATTN_OK
     assert bcheck(scale=0.0) == ea.ATTN_OK and bcheck(scale=-0.3) == ea.ATTN_OK
-    for d in (64, 128, 256):
+    for d in (32, 64, 96, 128, 160, 192, 224, 256):
         assert bcheck(d=d) == ea.ATTN_OK
     assert bcheck(Hkv=8) == ea.ATTN_OK and bcheck(Hkv=1) == ea.ATTN_OK
     assert bcheck(workspace_bytes=1 << 40) == ea.ATTN_OK
@@ -321,7 +324,7 @@ def test_bwd_invalid_arguments(over):
     assert bcheck(**over) == ea.ATTN_ERR_INVALID_ARG, over
 
 
-@pytest.mark.parametrize("d", [32, 80, 96, 192])
+@pytest.mark.parametrize("d", [16, 48, 80, 200, 288])
 def test_bwd_unsupported_head_dims(d):
     assert bcheck(d=d, workspace_bytes=1 << 30) == ea.ATTN_ERR_UNSUPPORTED
 

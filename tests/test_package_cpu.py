@@ -30,6 +30,7 @@ def test_tile_sweep_table():
         assert ts.DEFAULT[d] in variants, f"default of d={d} is not swept"
         names = [ts.variant_name(d, v) for v in variants]
         assert len(set(names)) == len(names)
+        row_chunks = 8 if d <= 64 else (16 if d <= 128 else 32)  # 16-byte chunks per (padded) LDS row
         for v in variants:
-            assert v["BN"] * (d // 8) % 256 == 0, "a tile must split evenly over 256 threads"
+            assert v["BN"] % 32 == 0 and v["BN"] * row_chunks % 256 == 0, "a tile must split evenly over 256 threads"
     assert {c[0] for c in ts.CASES} <= set(ts.VARIANTS)
