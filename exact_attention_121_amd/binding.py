@@ -54,6 +54,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         raise RuntimeError(
             f"{p} is missing: build it with `python -m exact_attention_121_amd.build` "
             "(or __graft_entry__.build()); there is no fallback path")
+    # PyTorch ships its own HIP runtime and asks for it under another file
+    # name than this library does (libamdhip64.so against libamdhip64.so.7,
+    # one soname).  Loaded first, torch's copy also satisfies this library;
+    # loaded after it, torch would bring a second runtime, whose streams this
+    # library's launches would then reject.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
