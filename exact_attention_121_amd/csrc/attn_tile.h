@@ -59,11 +59,12 @@ constexpr int query_blocks() {
   return D == 64 ? ATTN_QB64 : (D == 128 ? ATTN_QB128 : (D == 256 ? ATTN_QB256 : 1));
 }
 
-// Keys per K/V tile and matrix operands read ahead of their MFMA, per
-// head_dim.  The defaults (default_key_tile in attn_launch.h, k_ahead below)
-// are the measured best on gfx950; the offline tile sweep
-// (exact_attention_121_amd/tile_sweep.py) rebuilds the forward kernel with
-// other values through these hooks (0 = the default).
+// Keys per K/V tile, matrix operands read ahead of their MFMA and
+// workgroups per CU, per head_dim.  The defaults (default_key_tile and
+// default_wg_per_cu in attn_launch.h, k_ahead below) are the measured best on
+// gfx950; the offline tile sweep (exact_attention_121_amd/tile_sweep.py)
+// rebuilds the forward kernel with other values through these hooks (0 = the
+// default).
 #ifndef ATTN_BN32
 #define ATTN_BN32 0
 #endif
@@ -112,18 +113,51 @@ constexpr int query_blocks() {
 #ifndef ATTN_KAHEAD256
 #define ATTN_KAHEAD256 0
 #endif
+#ifndef ATTN_WG32
+#define ATTN_WG32 0
+#endif
+#ifndef ATTN_WG64
+#define ATTN_WG64 0
+#endif
+#ifndef ATTN_WG96
+#define ATTN_WG96 0
+#endif
+#ifndef ATTN_WG128
+#define ATTN_WG128 0
+#endif
+#ifndef ATTN_WG160
+#define ATTN_WG160 0
+#endif
+#ifndef ATTN_WG192
+#define ATTN_WG192 0
+#endif
+#ifndef ATTN_WG224
+#define ATTN_WG224 0
+#endif
+#ifndef ATTN_WG256
+#define ATTN_WG256 0
+#endif
 template <int D>
 constexpr int key_tile() {
   constexpr int hook = D == 32 ? ATTN_BN32 : D == 64 ? ATTN_BN64 : D == 96 ? ATTN_BN96 : D == 128 ? ATTN_BN128
                      : D == 160 ? ATTN_BN160 : D == 192 ? ATTN_BN192 : D == 224 ? ATTN_BN224 : ATTN_BN256;
   return hook ? hook : static_cast<int>(default_key_tile(D));
 }
+// Workgroups per CU the kernel is compiled for (its register budget).
+template <int D>
+constexpr int wg_per_cu() {
+  constexpr int hook = D == 32 ? ATTN_WG32 : D == 64 ? ATTN_WG64 : D == 96 ? ATTN_WG96 : D == 128 ? ATTN_WG128
+                     : D == 160 ? ATTN_WG160 : D == 192 ? ATTN_WG192 : D == 224 ? ATTN_WG224 : ATTN_WG256;
+  return hook ? hook : static_cast<int>(default_wg_per_cu(D));
+}
+// Operands read ahead: a longer run of them pays only with the register
+// budget of one workgroup per CU.
 template <int D>
 constexpr int k_ahead() {
   constexpr int hook = D == 32 ? ATTN_KAHEAD32 : D == 64 ? ATTN_KAHEAD64 : D == 96 ? ATTN_KAHEAD96
                      : D == 128 ? ATTN_KAHEAD128 : D == 160 ? ATTN_KAHEAD160 : D == 192 ? ATTN_KAHEAD192
                      : D == 224 ? ATTN_KAHEAD224 : ATTN_KAHEAD256;
-  return hook ? hook : (D <= 128 ? 4 : 6);
+  return hook ? hook : (wg_per_cu<D>() == 2 ? 4 : 6);
 }
 
 // 16-byte chunks per row of an LDS tile: the row's D / 8 chunks, padded to
@@ -148,7 +182,7 @@ struct Cfg {
   static constexpr int TILE_BYTES = BN * CPR * 16;   // one K (or V) tile in LDS
   static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
   // Workgroups per CU the register budget allows.
-  static constexpr int WG_PER_CU = QB == 1 ? static_cast<int>(default_wg_per_cu(D)) : 1;
+  static constexpr int WG_PER_CU = QB == 1 ? wg_per_cu<D>() : 1;
   // Matrix operands read from LDS ahead of their MFMA (K reads; twice as
   // many V transpose reads, two per MFMA).
   static constexpr int K_AHEAD = k_ahead<D>();

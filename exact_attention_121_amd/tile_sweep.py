@@ -12,8 +12,9 @@ per (head_dim, causal) case.
     (--dims 96,160 restricts either step to those head_dims)
 
 Choices swept (the compile-time hooks of csrc/attn_tile.h, per head_dim):
-keys per K/V tile (ATTN_BN*) and matrix operands read ahead of their MFMA
-(ATTN_KAHEAD*).  (64-row waves, ATTN_QB* = 2, are left out: one wave per
+keys per K/V tile (ATTN_BN*), matrix operands read ahead of their MFMA
+(ATTN_KAHEAD*) and, for head_dims above 128, workgroups per CU (ATTN_WG*:
+the register budget of 256 or 512 per lane).  (64-row waves, ATTN_QB* = 2, are left out: one wave per
 SIMD, 35-40 % slower where they fit, spilling where they do not.)  Only the
 forward translation unit is rebuilt; the decode and backward objects of the
 default build are linked unchanged (they keep the default tiles).
@@ -52,17 +53,20 @@ VARIANTS = {
     64: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
     96: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
     128: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
-    160: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64) for ka in (4, 6, 8)],
-    192: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64) for ka in (4, 6, 8)],
-    224: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64) for ka in (4, 6, 8)],
-    256: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64) for ka in (4, 6, 8)],
+    160: [dict(BN=bn, KAHEAD=ka, WG=wg) for bn in (32, 64) for ka in (4, 6, 8) for wg in (1, 2)],
+    192: [dict(BN=bn, KAHEAD=ka, WG=wg) for bn in (32, 64) for ka in (4, 6, 8) for wg in (1, 2)],
+    224: [dict(BN=bn, KAHEAD=ka, WG=wg) for bn in (32, 64) for ka in (4, 6, 8) for wg in (1, 2)],
+    256: [dict(BN=bn, KAHEAD=ka, WG=wg) for bn in (32, 64) for ka in (4, 6, 8) for wg in (1, 2)],
 }
-# The default build's choices (csrc/attn_launch.h default_key_tile, csrc/attn_tile.h k_ahead).
-DEFAULT = {d: dict(BN=64 if d <= 128 else 32, KAHEAD=4 if d <= 128 else 6) for d in VARIANTS}
+# The default build's choices (csrc/attn_launch.h default_key_tile and
+# default_wg_per_cu, csrc/attn_tile.h k_ahead).
+DEFAULT = {d: dict(BN=64 if d <= 128 else 32, KAHEAD=4 if d <= 224 else 6) for d in VARIANTS}
+for _d in (160, 192, 224, 256):
+    DEFAULT[_d]["WG"] = 2 if _d <= 224 else 1
 
 
 def variant_name(d: int, v: dict) -> str:
-    return f"d{d}_bn{v['BN']}_ka{v['KAHEAD']}"
+    return f"d{d}_bn{v['BN']}_ka{v['KAHEAD']}" + (f"_wg{v['WG']}" if "WG" in v else "")
 
 
 def _run(cmd):
@@ -91,6 +95,8 @@ def build_variants(jobs: int = 8, dims=None) -> list[str]:
         obj = os.path.join(SWEEP_DIR, f"fwd_{name}.o")
         lib = os.path.join(SWEEP_DIR, f"lib_{name}.so")
         flags = [f"-DATTN_BN{d}={v['BN']}", f"-DATTN_KAHEAD{d}={v['KAHEAD']}"]
+        if "WG" in v:
+            flags.append(f"-DATTN_WG{d}={v['WG']}")
         try:
             _run([hipcc, *hip_flags(flags), "-c", os.path.join(CSRC, "attn_fwd_kernel.hip"), "-o", obj])
             _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, *common, "-o", lib])
