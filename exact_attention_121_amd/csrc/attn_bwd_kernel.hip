@@ -138,42 +138,89 @@ __device__ __forceinline__ void p_and_ds(const STile<D>& arg, const STile<D>& dp
 template <int D>
 constexpr int bwd_dim_parts() { return D == 256 ? 2 : 1; }
 
+// Order of the dK/dV work inside a step: one 32-query sub-tile at a time
+// (SUB: fewer live registers, two workgroups per CU up to d = 128) or the
+// whole tile at once (more independent matrix work in flight per wave).
+// Measured on gfx950: sub-tiles are faster without the causal mask, except
+// at d = 256, once the grid gives every CU two workgroups; with the mask,
+// or on smaller grids, the whole tile is.
+template <int D, bool CAUSAL>
+constexpr bool bwd_dkdv_subtile_form() { return !CAUSAL && D != 256; }
+constexpr unsigned kDkdvSubtileMinGrid = 512;   // two workgroups for each of the 256 CUs
+
 // dK/dV workgroups per CU the register budget allows (K, V and the two
 // accumulators stay in registers).
-template <int D>
-constexpr int bwd_dkdv_wg_per_cu() { return D <= 64 ? 2 : 1; }
+template <int D, bool SUB>
+constexpr int bwd_dkdv_wg_per_cu() { return D <= (SUB ? 128 : 64) ? 2 : 1; }
 
 // dQ workgroups per CU (Q, dO and the dQ accumulators stay in registers).
 template <int D>
 constexpr int bwd_dq_wg_per_cu() { return D <= 128 ? 2 : 1; }
 
-// pv_tile over NDT of the 32-dim output tiles, whose transpose-read lane
-// offsets are in voff (the dims of those tiles only).
+// P and dS of one 32-query sub-tile from its scores s and dP (no mask):
+// entry r is query 8 (r / 4) + r % 4 past the lane's first, whose LSE (log2)
+// and Delta lse and delta point at in LDS; P = exp2(c s - lse) and dS =
+// P (dP - delta), rounded to T.
+template <typename T>
+__device__ __forceinline__ void p_ds_subtile(const f32x16& s, const f32x16& dp, const float* lse, const float* delta,
+                                             float c, half8 (&pf)[2], half8 (&dsf)[2]) {
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const float4 l4 = *reinterpret_cast<const float4*>(lse + 8 * rr);
+    const float4 d4 = *reinterpret_cast<const float4*>(delta + 8 * rr);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * rr + i;
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[i]));
+      pf[r >> 3][r & 7] = to_elem<T>(pv);
+      dsf[r >> 3][r & 7] = to_elem<T>(pv * (dp[r] - dv[i]));
+    }
+  }
+}
+
+// Sub-tile t of a stage (its 32 rows 32 t .. 32 t + 31, from LDS) times the
+// wave's fragments (B operands, 32 columns): S_t = Q_t K^T or dP_t = dO_t V^T.
+template <int D, typename T>
+__device__ __forceinline__ f32x16 rows_times_frags(const char* stage, const QFrag<D>& frags, const Offsets<D>& off,
+                                                   int t) {
+  using C = Cfg<D>;
+  f32x16 acc = {};
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) {
+    const half8 a = *reinterpret_cast<const half8*>(stage + off.kofs(dc) + 32 * t * C::CPR * 16);
+    acc = mfma16<T>(a, frags[0][dc], acc);
+  }
+  return acc;
+}
+
+// acc[i] += (sub-tile t of a stage)^T p over NDT 32-dim output tiles: the
+// transposed rows 32 t .. 32 t + 31 as A operands (transpose reads at the
+// lane offsets voff), p (the sub-tile's P or dS) as B operands.
 template <int D, int NDT, typename T>
-__device__ __forceinline__ void pv_tile_part(const char* vs, const PTile<D>& pf, const int (&voff)[2][NDT],
-                                             f32x16 (&acc)[NDT]) {
+__device__ __forceinline__ void tr_times_p(const char* stage, const half8 (&p)[2], const int (&voff)[2][NDT], int t,
+                                           f32x16 (&acc)[NDT]) {
   using C = Cfg<D>;
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t)
+  for (int h = 0; h < 2; ++h) {
+    const int kb = (32 * t + 16 * h) * C::CPR * 16;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kb = (32 * t + 16 * h) * C::CPR * 16;
-#pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const short4v lo = tr_read(vs + voff[0][i] + kb);
-        const short4v hi = tr_read(vs + voff[1][i] + kb);
-        const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[i] = mfma16<T>(a, pf[0][t][h], acc[i]);
-      }
+    for (int i = 0; i < NDT; ++i) {
+      const short4v lo = tr_read(stage + voff[0][i] + kb);
+      const short4v hi = tr_read(stage + voff[1][i] + kb);
+      const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[i] = mfma16<T>(a, p[h], acc[i]);
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV.  Query tiles of BN rows stream through LDS (Q in the "K" stages,
 // dO in the "V" stages); the wave's 32 keys are the columns of S and dP.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, typename T>
-__global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dkdv_kernel(BwdParams p, int k_tiles) {
+template <int D, bool CAUSAL, bool SUB, typename T>
+__global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn_bwd_dkdv_kernel(BwdParams p, int k_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-key block per wave");
   // Q stages 0/1, dO stages 0/1, then per stage the tile's LSE (log2) and
@@ -276,52 +323,75 @@ __global__ __launch_bounds__(kThreads, bwd_dkdv_wg_per_cu<D>()) void attn_bwd_dk
     const bool active = kw0 < N && !(CAUSAL && q0 + C::BN - 1 < kw0);
     issue(u + 1, st ^ 1);
     if (active) {
-      // Per-entry LSE and Delta from LDS: entry r of sub-tile t is query
-      // q0 + 32 t + 8 (r / 4) + 4 g + r % 4.
-      const float* lrow = rowterms + (2 * st) * 64;
-      const float* drow = rowterms + (2 * st + 1) * 64;
-      float lse2[C::NT][16], delta[C::NT][16];
+      const float* lrow = rowterms + (2 * st) * 64;   // LSE (log2) of the tile's queries
+      const float* drow = rowterms + (2 * st + 1) * 64;   // Delta of the tile's queries
+      if constexpr (SUB) {
+        // One 32-query sub-tile t at a time: S_t and dP_t, then P_t and
+        // dS_t, then their products, so that only one sub-tile's scores and
+        // LSE / Delta are live.  Entry r of sub-tile t is query
+        // q0 + 32 t + 8 (r / 4) + 4 g + r % 4.
 #pragma unroll
-      for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float4 l4 = *reinterpret_cast<const float4*>(lrow + 32 * t + 8 * rr + 4 * g);
-          const float4 d4 = *reinterpret_cast<const float4*>(drow + 32 * t + 8 * rr + 4 * g);
-          lse2[t][4 * rr + 0] = l4.x;
-          lse2[t][4 * rr + 1] = l4.y;
-          lse2[t][4 * rr + 2] = l4.z;
-          lse2[t][4 * rr + 3] = l4.w;
-          delta[t][4 * rr + 0] = d4.x;
-          delta[t][4 * rr + 1] = d4.y;
-          delta[t][4 * rr + 2] = d4.z;
-          delta[t][4 * rr + 3] = d4.w;
+        for (int t = 0; t < C::NT; ++t) {
+          const f32x16 s = rows_times_frags<D, T>(k_stage<D>(smem, st), kf, off, t);   // S_t = Q_t K^T
+          const f32x16 dp = rows_times_frags<D, T>(v_stage<D>(smem, st), vf, off, t);  // dP_t = dO_t V^T
+          half8 pf[2], dsf[2];
+          p_ds_subtile<T>(s, dp, lrow + 32 * t + 4 * g, drow + 32 * t + 4 * g, p.c, pf, dsf);
+          tr_times_p<D, NDT, T>(v_stage<D>(smem, st), pf, voff, t, dv_acc);    // dV^T += dO_t^T P_t
+          tr_times_p<D, NDT, T>(k_stage<D>(smem, st), dsf, voff, t, dk_acc);   // dK^T += Q_t^T dS_t
         }
-      STile<D> s, dp;
-      qk_tile<D, T>(k_stage<D>(smem, st), kf, off, s);    // S = Q K^T: rows queries, columns keys
-      qk_tile<D, T>(v_stage<D>(smem, st), vf, off, dp);   // dP = dO V^T
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[0][t][r] = __builtin_fmaf(s[0][t][r], p.c, -lse2[t][r]);
-      if (CAUSAL && q0 < kw0 + 31) {
+      } else {
+        // The whole tile at once: S and dP of every sub-tile, the causal
+        // mask on tiles that cross the wave's diagonal, then P and dS and
+        // their products.
+        float lse2[C::NT][16], delta[C::NT][16];
 #pragma unroll
         for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qrow = q0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            s[0][t][r] = key <= qrow ? s[0][t][r] : -INFINITY;
+          for (int rr = 0; rr < 4; ++rr) {
+            const float4 l4 = *reinterpret_cast<const float4*>(lrow + 32 * t + 8 * rr + 4 * g);
+            const float4 d4 = *reinterpret_cast<const float4*>(drow + 32 * t + 8 * rr + 4 * g);
+            lse2[t][4 * rr + 0] = l4.x;
+            lse2[t][4 * rr + 1] = l4.y;
+            lse2[t][4 * rr + 2] = l4.z;
+            lse2[t][4 * rr + 3] = l4.w;
+            delta[t][4 * rr + 0] = d4.x;
+            delta[t][4 * rr + 1] = d4.y;
+            delta[t][4 * rr + 2] = d4.z;
+            delta[t][4 * rr + 3] = d4.w;
           }
+        STile<D> s, dp;
+        qk_tile<D, T>(k_stage<D>(smem, st), kf, off, s);    // S = Q K^T: rows queries, columns keys
+        qk_tile<D, T>(v_stage<D>(smem, st), vf, off, dp);   // dP = dO V^T
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[0][t][r] = __builtin_fmaf(s[0][t][r], p.c, -lse2[t][r]);
+        if (CAUSAL && q0 < kw0 + 31) {
+#pragma unroll
+          for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qrow = q0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+              s[0][t][r] = key <= qrow ? s[0][t][r] : -INFINITY;
+            }
+        }
+        PTile<D> pf, dsf;
+        p_and_ds<D, T>(s, dp, delta, pf, dsf);
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t) {
+          tr_times_p<D, NDT, T>(v_stage<D>(smem, st), pf[0][t], voff, t, dv_acc);    // dV^T += dO^T P
+        }
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t) {
+          tr_times_p<D, NDT, T>(k_stage<D>(smem, st), dsf[0][t], voff, t, dk_acc);   // dK^T += Q^T dS
+        }
       }
-      PTile<D> pf, dsf;
-      p_and_ds<D, T>(s, dp, delta, pf, dsf);
-      pv_tile_part<D, NDT, T>(v_stage<D>(smem, st), pf, voff, dv_acc);    // dV^T += dO^T P
-      pv_tile_part<D, NDT, T>(k_stage<D>(smem, st), dsf, voff, dk_acc);   // dK^T += Q^T dS
     }
     wait_vm_all();
     __syncthreads();
     };
-  if constexpr (D <= 64) {
-    // Unrolled, these head_dims no longer fit two workgroups per CU.
+  if constexpr (bwd_dkdv_wg_per_cu<D, SUB>() == 2) {
+    // Unrolled, the step no longer fits two workgroups per CU.
     for (int u = 0; u < steps; ++u) step(u & 1, u);
   } else {
     for (int u = 0; u < steps; u += 2) {
@@ -477,9 +547,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int k_tiles = (a.N + kBwdKeys - 1) / kBwdKeys;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, T>),
-                     dim3(static_cast<unsigned>(a.B) * a.Hkv * k_tiles * bwd_dim_parts<D>()), dim3(kThreads), 0, s,
-                     p, k_tiles);
+  const unsigned dkdv_grid = static_cast<unsigned>(a.B) * a.Hkv * k_tiles * bwd_dim_parts<D>();
+  if (bwd_dkdv_subtile_form<D, CAUSAL>() && dkdv_grid >= kDkdvSubtileMinGrid)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, bwd_dkdv_subtile_form<D, CAUSAL>(), T>), dim3(dkdv_grid),
+                       dim3(kThreads), 0, s, p, k_tiles);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, false, T>), dim3(dkdv_grid), dim3(kThreads), 0, s, p, k_tiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int q_tiles = (a.N + C::BM - 1) / C::BM;

@@ -137,3 +137,21 @@ def test_gqa_workload_backward_one_group():
     got = gpu_backward(q, k, v, do, w.scale, w.causal)
     ref = attention_bwd_ref(q[:, 0:4], k[:, 0:1], v[:, 0:1], do[:, 0:4], w.scale, causal=w.causal)
     assert_grad_parity([got[0][:, 0:4], got[1][:, 0:1], got[2][:, 0:1]], ref, "gqa_causal group 0")
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 160, 192, 224])
+def test_backward_subtile_form(d):
+    """Non-causal problems whose dK/dV grid gives every CU two workgroups
+    (here exactly 512: B=4, Hkv=16, 8 key tiles of 128) run the dK/dV kernel
+    that takes each 64-query tile in two 32-query halves; the smaller grids
+    above run the whole-tile form.  The oracle checks two whole heads."""
+    B, H, N = 4, 16, 1000
+    _say(f"[bwd] sub-tile form B={B} H={H} N={N} d={d}")
+    q, k, v = make_qkv(B, H, H, N, d, seed=2100 + d)
+    do = make_dout(q.shape, seed=2200 + d)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = gpu_backward(q, k, v, do, scale, False)
+    for b, h in ((0, 0), (3, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = attention_bwd_ref(q[sl], k[sl], v[sl], do[sl], scale, causal=False)
+        assert_grad_parity([x[sl] for x in got], ref, f"sub-tile form d={d} head ({b}, {h})")
