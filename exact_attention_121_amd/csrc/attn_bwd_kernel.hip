@@ -182,14 +182,13 @@ __device__ __forceinline__ void p_ds_subtile(const f32x16& s, const f32x16& dp, 
 
 // Sub-tile t of a stage (its 32 rows 32 t .. 32 t + 31, from LDS) times the
 // wave's fragments (B operands, 32 columns): S_t = Q_t K^T or dP_t = dO_t V^T.
-template <int D, typename T>
-__device__ __forceinline__ f32x16 rows_times_frags(const char* stage, const QFrag<D>& frags, const Offsets<D>& off,
-                                                   int t) {
+template <int D, typename T, typename KO>
+__device__ __forceinline__ f32x16 rows_times_frags(const char* stage, const QFrag<D>& frags, const KO& kofs, int t) {
   using C = Cfg<D>;
   f32x16 acc = {};
 #pragma unroll
   for (int dc = 0; dc < C::DC; ++dc) {
-    const half8 a = *reinterpret_cast<const half8*>(stage + off.kofs(dc) + 32 * t * C::CPR * 16);
+    const half8 a = *reinterpret_cast<const half8*>(stage + kofs(dc) + 32 * t * C::CPR * 16);
     acc = mfma16<T>(a, frags[0][dc], acc);
   }
   return acc;
@@ -197,9 +196,9 @@ __device__ __forceinline__ f32x16 rows_times_frags(const char* stage, const QFra
 
 // acc[i] += (sub-tile t of a stage)^T p over NDT 32-dim output tiles: the
 // transposed rows 32 t .. 32 t + 31 as A operands (transpose reads at the
-// lane offsets voff), p (the sub-tile's P or dS) as B operands.
-template <int D, int NDT, typename T>
-__device__ __forceinline__ void tr_times_p(const char* stage, const half8 (&p)[2], const int (&voff)[2][NDT], int t,
+// lane offsets voff(key group, i)), p (the sub-tile's P or dS) as B operands.
+template <int D, int NDT, typename T, typename VO>
+__device__ __forceinline__ void tr_times_p(const char* stage, const half8 (&p)[2], const VO& voff, int t,
                                            f32x16 (&acc)[NDT]) {
   using C = Cfg<D>;
 #pragma unroll
@@ -207,8 +206,8 @@ __device__ __forceinline__ void tr_times_p(const char* stage, const half8 (&p)[2
     const int kb = (32 * t + 16 * h) * C::CPR * 16;
 #pragma unroll
     for (int i = 0; i < NDT; ++i) {
-      const short4v lo = tr_read(stage + voff[0][i] + kb);
-      const short4v hi = tr_read(stage + voff[1][i] + kb);
+      const short4v lo = tr_read(stage + voff(0, i) + kb);
+      const short4v hi = tr_read(stage + voff(1, i) + kb);
       const half8 a = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[i] = mfma16<T>(a, p[h], acc[i]);
     }
@@ -261,9 +260,11 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
   }
   Offsets<D> off;
   off.init(lane);
-  // Transpose-read offsets of this workgroup's output dims (as Offsets::init).
-  int voff[2][NDT];
-  {
+  // Transpose-read offsets of this workgroup's output dims: the Offsets
+  // registers when one workgroup covers all dims; with the dims split over
+  // NP workgroups, those of this workgroup's part (as Offsets::init).
+  int vpart[NP == 1 ? 1 : 2][NP == 1 ? 1 : NDT];
+  if constexpr (NP > 1) {
     const int m16 = lane & 15;
     const int dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);
 #pragma unroll
@@ -271,9 +272,11 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
 #pragma unroll
       for (int i = 0; i < NDT; ++i) {
         const int dim = 32 * (part * NDT + i) + dsub;
-        voff[hi][i] = swz<D>(4 * g + (m16 >> 2) + 8 * hi, dim >> 3) + (dim & 7) * 2;
+        vpart[hi][i] = swz<D>(4 * g + (m16 >> 2) + 8 * hi, dim >> 3) + (dim & 7) * 2;
       }
   }
+  auto voff = [&](int hi, int i) { return NP == 1 ? off.vofs(hi, i) : vpart[NP == 1 ? 0 : hi][NP == 1 ? 0 : i]; };
+  auto kofs = [&](int dc) { return off.kofs(dc); };
   LoadOffsets<D> lo;
   lo.init(tid);
 
@@ -332,8 +335,8 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
         // q0 + 32 t + 8 (r / 4) + 4 g + r % 4.
 #pragma unroll
         for (int t = 0; t < C::NT; ++t) {
-          const f32x16 s = rows_times_frags<D, T>(k_stage<D>(smem, st), kf, off, t);   // S_t = Q_t K^T
-          const f32x16 dp = rows_times_frags<D, T>(v_stage<D>(smem, st), vf, off, t);  // dP_t = dO_t V^T
+          const f32x16 s = rows_times_frags<D, T>(k_stage<D>(smem, st), kf, kofs, t);   // S_t = Q_t K^T
+          const f32x16 dp = rows_times_frags<D, T>(v_stage<D>(smem, st), vf, kofs, t);  // dP_t = dO_t V^T
           half8 pf[2], dsf[2];
           p_ds_subtile<T>(s, dp, lrow + 32 * t + 4 * g, drow + 32 * t + 4 * g, p.c, pf, dsf);
           tr_times_p<D, NDT, T>(v_stage<D>(smem, st), pf, voff, t, dv_acc);    // dV^T += dO_t^T P_t

@@ -218,13 +218,20 @@ constexpr uint32_t kPadChunk = 0x80000000u;
 // thread `tid` copies into a swizzled tile (the chunk that belongs at
 // position p % CPR of row p / CPR of the tile, or kPadChunk for a padding
 // slot).
+// Load i of a thread covers tile row p / CPR with p = i * 256 + tid, so the
+// row advances by 256 / CPR per load; the swizzle depends only on a row's
+// low four bits, so the offsets repeat, a whole number of rows further on,
+// every kPeriod loads and only kPeriod of them are kept (at(i) adds the rows).
 template <int D>
 struct LoadOffsets {
-  uint32_t src[Cfg<D>::LOADS];
+  using C = Cfg<D>;
+  static constexpr int kRowsPerLoad = kThreads / C::CPR;
+  static constexpr int kPeriod = kRowsPerLoad >= 16 ? 1 : 16 / kRowsPerLoad;
+  static constexpr int kKept = kPeriod < C::LOADS ? kPeriod : C::LOADS;
+  uint32_t src[kKept];
   __device__ __forceinline__ void init(int tid) {
-    using C = Cfg<D>;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
+    for (int i = 0; i < kKept; ++i) {
       const int p = i * kThreads + tid;  // destination chunk; lanes of a wave are consecutive
       const int row = p / C::CPR;
       const int chunk = (swz<D>(row, p % C::CPR) >> 4) - row * C::CPR;
@@ -233,6 +240,11 @@ struct LoadOffsets {
       else
         src[i] = chunk < C::SRC_CPR ? static_cast<uint32_t>((row * D + chunk * 8) * 2) : kPadChunk;
     }
+  }
+  // i compile-time in the unrolled loads: a register plus a constant.  A
+  // padding slot stays at or above 2^31 (kPadChunk plus rows of the tile).
+  __device__ __forceinline__ uint32_t at(int i) const {
+    return src[i % kPeriod] + static_cast<uint32_t>((i / kPeriod) * kPeriod * kRowsPerLoad * D * 2);
   }
 };
 
@@ -252,7 +264,7 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, char* til
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     char* dst = tile + (i * kThreads + (tid & ~63)) * 16;  // wave-uniform base
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, static_cast<int>(base + lo.src[i]),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, static_cast<int>(base + lo.at(i)),
                                              0, 0, 0);
   }
 }
@@ -281,25 +293,31 @@ __device__ __forceinline__ float xlane_sum(float x) {
 
 // Per-lane LDS byte offsets of the matrix operands inside a (swizzled) tile.
 // Tile rows 32*t + 16*h (K) or key groups (V) only add a constant, so every
-// operand read is one of these registers plus an immediate offset.  In rows
-// of 32 chunks the swizzle changes only the low four bits of the chunk
-// index, so chunk c + 16 lies 256 bytes after chunk c: the upper half of the
-// dims reuses the lower half's registers with an immediate offset.
+// operand read is one of these registers plus an immediate offset.  Two
+// identities of the swizzle save registers:
+//  * in rows of 32 chunks it changes only the low four bits of the chunk
+//    index, so chunk c + 16 lies 256 bytes after chunk c: the upper half of
+//    the dims reuses the lower half's registers;
+//  * with the 16-entry map, row r + 8 XORs with f(r) ^ 8, so key group 1
+//    (rows + 8) of row tile dt reads where group 0 of row tile dt ^ 2 does,
+//    8 rows further on (when the row tiles come in fours).
 template <int D>
 struct Offsets {
   using C = Cfg<D>;
   static constexpr bool kHalves = C::CPR == 32;
   static constexpr int KR = kHalves && C::DC > 8 ? 8 : C::DC;  // registers for K chunks
   static constexpr int VR = kHalves && C::DT > 4 ? 4 : C::DT;  // registers for V row tiles
+  static constexpr bool kGroup1FromGroup0 = C::CPR >= 16 && VR % 4 == 0;
+  static constexpr int VG = kGroup1FromGroup0 ? 1 : 2;         // key groups with registers
   int k[KR];       // K rows lane%32 (+32 t), chunk 2 dc + lane/32
-  int v[2][VR];    // V keys 4 g + (lane%16)/4 (+8 for [1]), dims of row tile dt
+  int v[VG][VR];   // V keys 4 g + (lane%16)/4 (+8 for [1]), dims of row tile dt
   __device__ __forceinline__ void init(int lane) {
     const int lr = lane & 31, g = lane >> 5, m16 = lane & 15;
 #pragma unroll
     for (int dc = 0; dc < KR; ++dc) k[dc] = swz<D>(lr, 2 * dc + g);
     const int dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);  // dim offset inside a 32-dim tile
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi)
+    for (int hi = 0; hi < VG; ++hi)
 #pragma unroll
       for (int dt = 0; dt < VR; ++dt) {
         const int dim = 32 * dt + dsub;
@@ -309,7 +327,11 @@ struct Offsets {
   // Offset of K chunk pair dc and of V row tile dt (dc, dt compile-time in
   // the unrolled loops, so the choice and the +256 fold away).
   __device__ __forceinline__ int kofs(int dc) const { return dc < KR ? k[dc] : k[dc - 8] + 256; }
-  __device__ __forceinline__ int vofs(int hi, int dt) const { return dt < VR ? v[hi][dt] : v[hi][dt - 4] + 256; }
+  __device__ __forceinline__ int vofs(int hi, int dt) const {
+    if (dt >= VR) return vofs(hi, dt - 4) + 256;
+    if (kGroup1FromGroup0 && hi == 1) return v[0][dt ^ 2] + 8 * C::CPR * 16;
+    return v[kGroup1FromGroup0 ? 0 : hi][dt];
+  }
 };
 
 template <int D>
