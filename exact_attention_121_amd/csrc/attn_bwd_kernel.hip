@@ -26,6 +26,9 @@
 //     cores, P and dS on the vector ALUs, then dV^T += dO^T P and
 //     dK^T += Q^T dS with P and dS used straight from registers and the
 //     transposed tiles read with ds_read_b64_tr_b16 (the forward's P.V step).
+//     Two forms of that step, chosen at launch: the whole tile at once, or
+//     one 32-query half at a time, which keeps fewer registers live and runs
+//     two workgroups per CU (non-causal grids of two workgroups per CU).
 //   * attn_bwd_dq_kernel: one workgroup per 128 query rows, shaped like the
 //     forward kernel: S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T.
 // The two main kernels recompute S and dP each; there are no atomics, and
