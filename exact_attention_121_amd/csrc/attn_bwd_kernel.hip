@@ -156,9 +156,11 @@ constexpr unsigned kDkdvSubtileMinGrid = 512;   // two workgroups for each of th
 template <int D, bool SUB>
 constexpr int bwd_dkdv_wg_per_cu() { return D <= (SUB ? 128 : 64) ? 2 : 1; }
 
-// dQ workgroups per CU (Q, dO and the dQ accumulators stay in registers).
+// dQ workgroups per CU (Q, dO and the dQ accumulators stay in registers):
+// two fit without spilling up to d = 160 (at d = 192 the spill cost the
+// causal and small grids 7-9 %).
 template <int D>
-constexpr int bwd_dq_wg_per_cu() { return D <= 128 ? 2 : 1; }
+constexpr int bwd_dq_wg_per_cu() { return D <= 160 ? 2 : 1; }
 
 // P and dS of one 32-query sub-tile from its scores s and dP (no mask):
 // entry r is query 8 (r / 4) + r % 4 past the lane's first, whose LSE (log2)
