@@ -340,6 +340,10 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
         // q0 + 32 t + 8 (r / 4) + 4 g + r % 4.
 #pragma unroll
         for (int t = 0; t < C::NT; ++t) {
+          // Keep the scheduler from hoisting sub-tile t's operand reads into
+          // sub-tile t - 1, which lengthens register lifetimes (at d = 128
+          // the spill falls from 52 to 36 bytes per lane; 4 % faster).
+          __builtin_amdgcn_sched_barrier(0);
           const f32x16 s = rows_times_frags<D, T>(k_stage<D>(smem, st), kf, kofs, t);   // S_t = Q_t K^T
           const f32x16 dp = rows_times_frags<D, T>(v_stage<D>(smem, st), vf, kofs, t);  // dP_t = dO_t V^T
           half8 pf[2], dsf[2];
