@@ -42,6 +42,10 @@
  *     owned by the caller, which keeps it alive until the work queued on
  *     `stream` has completed.  The library allocates nothing and keeps no
  *     state between calls; calls from several host threads are safe.
+ *   - Graphs: the entry points queue kernel launches only (no allocation,
+ *     no memset, no copy), so a call can be captured in a HIP graph on
+ *     `stream` and replayed; a replay reads the captured buffers' current
+ *     contents.
  *   - Asynchrony: attn_fwd only queues work on `stream` (NULL = the default
  *     stream) and returns; it never synchronises.  A device fault surfaces at
  *     the caller's next synchronisation.
