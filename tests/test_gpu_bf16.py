@@ -168,3 +168,21 @@ def test_decode_bf16(shape, d):
         torch.cuda.synchronize()
         O_ref, L_ref = attention_decode_ref(q, k, v, float(np.float32(1 / np.sqrt(d))), causal=causal)
         check(o.float().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, f"decode {shape} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 96, 160, 224])
+def test_backward_bf16_subtile_form(d):
+    """bf16 gradients from the sub-tile form of the dK/dV kernel (non-causal,
+    a grid of 512 dK/dV workgroups: B=4, H=16, N=1000); the oracle checks two
+    whole heads."""
+    from oracle.backward import attention_bwd_ref
+    B, H, N = 4, 16, 1000
+    _say(f"[bf16 bwd] sub-tile form B={B} H={H} N={N} d={d}")
+    q, k, v = make_qkv_bf16(B, H, H, N, d, seed=2300 + d)
+    do = _bf16_dout(q.shape, 2400 + d)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = gpu_backward_bf16(q, k, v, do, scale, False)
+    for b, h in ((0, 0), (3, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = attention_bwd_ref(q[sl], k[sl], v[sl], do[sl], scale, causal=False)
+        check_grads([x[sl] for x in got], ref, f"sub-tile form d={d} head ({b}, {h})")
