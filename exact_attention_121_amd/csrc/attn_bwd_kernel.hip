@@ -379,13 +379,14 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[0][t][r] = __builtin_fmaf(s[0][t][r], p.c, -lse2[t][r]);
         if (CAUSAL && q0 < kw0 + 31) {
+          // Entry r of sub-tile t is query q0 + 4 g + (32 t + 8 (r / 4) +
+          // r % 4): visible iff that constant offset reaches key - q0 - 4 g.
+          const int first = key - q0 - 4 * g;
 #pragma unroll
           for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qrow = q0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-              s[0][t][r] = key <= qrow ? s[0][t][r] : -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+              s[0][t][r] = 32 * t + 8 * (r >> 2) + (r & 3) >= first ? s[0][t][r] : -INFINITY;
         }
         PTile<D> pf, dsf;
         p_and_ds<D, T>(s, dp, delta, pf, dsf);

@@ -388,20 +388,22 @@ __device__ __forceinline__ void qk_tile(const char* ks, const QFrag<D>& qf, cons
 
 // Keys past the end of the sequence, or after the query when causal, get
 // logit -inf (then exp2 gives exactly 0).  Lane L holds keys
-// 32 t + 8 (r/4) + 4 (L/32) + r%4 of query row `qrow` (+32 per block).
+// 32 t + 8 (r/4) + 4 (L/32) + r%4 of query row `qrow` (+32 per block): the
+// last visible key gives the lane one limit, and each entry's key offset
+// 32 t + 8 (r/4) + r%4 is a compile-time constant compared with it.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void mask_tile(STile<D>& s, int kv0, int N, int qrow, int g) {
   using C = Cfg<D>;
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb)
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int last = CAUSAL ? min(N - 1, qrow + 32 * qb) : N - 1;   // last visible key of the row
+    const int lim = last - kv0 - 4 * g;
 #pragma unroll
     for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = key < N && (!CAUSAL || key <= qrow + 32 * qb);
-        s[qb][t][r] = ok ? s[qb][t][r] : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        s[qb][t][r] = 32 * t + 8 * (r >> 2) + (r & 3) <= lim ? s[qb][t][r] : -INFINITY;
+  }
 }
 
 // Row maxima of a tile's raw logits, in log2 units (c > 0).
