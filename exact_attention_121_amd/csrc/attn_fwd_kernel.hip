@@ -79,7 +79,7 @@ struct Params {
 };
 
 template <int D, bool CAUSAL, typename T>
-__global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
   // K stages 0/1 then V stages 0/1.
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];

@@ -150,6 +150,18 @@ constexpr int wg_per_cu() {
                      : D == 160 ? ATTN_WG160 : D == 192 ? ATTN_WG192 : D == 224 ? ATTN_WG224 : ATTN_WG256;
   return hook ? hook : static_cast<int>(default_wg_per_cu(D));
 }
+// Workgroups per CU of the forward kernel: as above, except that without a
+// hook causal d = 256 takes two (a 76-byte spill per lane, but the second
+// wave per SIMD hides more of the causal kernel's latency: +3-5 % measured;
+// without the mask two are 5 % slower).  The decode kernel keeps one: its
+// split plan follows default_wg_per_cu.
+template <int D, bool CAUSAL>
+constexpr int fwd_wg_per_cu() {
+  constexpr int hook = D == 32 ? ATTN_WG32 : D == 64 ? ATTN_WG64 : D == 96 ? ATTN_WG96 : D == 128 ? ATTN_WG128
+                     : D == 160 ? ATTN_WG160 : D == 192 ? ATTN_WG192 : D == 224 ? ATTN_WG224 : ATTN_WG256;
+  if (query_blocks<D>() != 1) return 1;
+  return hook ? hook : (D == 256 && CAUSAL ? 2 : static_cast<int>(default_wg_per_cu(D)));
+}
 // Operands read ahead: a longer run of them pays only with the register
 // budget of one workgroup per CU.
 template <int D>

@@ -62,7 +62,7 @@ VARIANTS = {
 # default_wg_per_cu, csrc/attn_tile.h k_ahead).
 DEFAULT = {d: dict(BN=64 if d <= 128 else 32, KAHEAD=4 if d <= 224 else 6) for d in VARIANTS}
 for _d in (160, 192, 224, 256):
-    DEFAULT[_d]["WG"] = 2 if _d <= 224 else 1
+    DEFAULT[_d]["WG"] = 2   # d = 256: the default of the causal kernel (the swept case); non-causal d = 256 takes 1
 
 
 def variant_name(d: int, v: dict) -> str:
