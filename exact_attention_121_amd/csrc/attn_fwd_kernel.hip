@@ -56,6 +56,9 @@
 //     stay <= 256; row sums add the fp16 probabilities with v_dot2.
 //   * Causal: key tiles entirely above a wave's diagonal are skipped; only
 //     tiles crossing the diagonal or the end of the sequence are masked.
+//   * Epilogue: each wave writes its 32 normalised rows to an LDS region of
+//     its own and reads them back row-contiguous, so that O leaves in fully
+//     coalesced 16-byte-per-lane stores instead of 8-byte pieces of 32 rows.
 //   * Workgroup ids are remapped so that each of the 8 XCDs (each with its
 //     own L2) receives a contiguous range of (head, query tile) work, i.e. the
 //     query tiles of the same heads share their K/V in one L2; causal query
@@ -174,26 +177,19 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
     if (j + 1 < nt) pipeline_step<D, CAUSAL, 1, T>(j + 1, nt, smem, krs, vrs, lo, tid, w, sb, sa);
   }
 
-  // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
+  // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).  After the loop's last
+  // barrier no copy or read uses the K/V stages any more, so each wave
+  // stages its rows for a coalesced store in an LDS region of its own.
+  static_assert(kWaves * 32 * C::CPR * 16 <= 4 * C::TILE_BYTES, "output staging must fit the K/V stages");
+  char* region = smem + wv * (32 * C::CPR * 16);
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     const int row = w.qrow + 32 * qb;
+    const int row0 = w.qw0 + 32 * qb;
     const float l_tot = xlane_sum(w.l_run[qb]);
-    if (row < N) {
-      const float inv = 1.0f / l_tot;
-      _Float16* __restrict__ orow = p.o + qoff + (size_t)row * D;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          half4 h;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = to_elem<T>(w.oacc[qb][dt][4 * rq + i] * inv);
-          *reinterpret_cast<half4*>(orow + 32 * dt + 8 * rq + 4 * w.g) = h;
-        }
-      if (p.lse != nullptr && w.g == 0)
-        p.lse[((size_t)b * p.Hq + hq) * N + row] = (w.m_run[qb] + __builtin_log2f(l_tot)) * kLn2;
-    }
+    store_o_rows<D, T>(region, w.oacc[qb], 1.0f / l_tot, p.o + qoff + (size_t)row0 * D, N - row0, lane);
+    if (p.lse != nullptr && w.g == 0 && row < N)
+      p.lse[((size_t)b * p.Hq + hq) * N + row] = (w.m_run[qb] + __builtin_log2f(l_tot)) * kLn2;
   }
 }
 
