@@ -413,23 +413,11 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
     }
   }
 
-  if (key >= N) return;
-  _Float16* __restrict__ dkrow = p.dk + kvoff + (size_t)key * D;
-  _Float16* __restrict__ dvrow = p.dv + kvoff + (size_t)key * D;
-#pragma unroll
-  for (int i = 0; i < NDT; ++i)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      half4 hk, hv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hk[e] = to_elem<T>(dk_acc[i][4 * rq + e] * p.scale);
-        hv[e] = to_elem<T>(dv_acc[i][4 * rq + e]);
-      }
-      const int dim0 = 32 * (part * NDT + i) + 8 * rq + 4 * g;
-      *reinterpret_cast<half4*>(dkrow + dim0) = hk;
-      *reinterpret_cast<half4*>(dvrow + dim0) = hv;
-    }
+  // The loop's last barrier freed the stages: each wave stages its rows of
+  // dK and then dV there for coalesced stores.
+  char* region = row_region<D>(smem, wv);
+  store_rows<D, T, NDT>(region, dk_acc, p.scale, p.dk + kvoff + (size_t)kw0 * D + 32 * part * NDT, N - kw0, lane);
+  store_rows<D, T, NDT>(region, dv_acc, 1.0f, p.dv + kvoff + (size_t)kw0 * D + 32 * part * NDT, N - kw0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -536,17 +524,8 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
     if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
-  if (row >= N) return;
-  _Float16* __restrict__ out = p.dq + qoff + (size_t)row * D;
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      half4 h;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = to_elem<T>(dq_acc[0][dt][4 * rq + i] * p.scale);
-      *reinterpret_cast<half4*>(out + 32 * dt + 8 * rq + 4 * g) = h;
-    }
+  // As in the forward: rows staged in the freed stages, coalesced stores.
+  store_rows<D, T>(row_region<D>(smem, wv), dq_acc[0], p.scale, p.dq + qoff + (size_t)qw0 * D, N - qw0, lane);
 }
 
 template <int D, bool CAUSAL, typename T>

@@ -180,14 +180,13 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).  After the loop's last
   // barrier no copy or read uses the K/V stages any more, so each wave
   // stages its rows for a coalesced store in an LDS region of its own.
-  static_assert(kWaves * 32 * C::CPR * 16 <= 4 * C::TILE_BYTES, "output staging must fit the K/V stages");
-  char* region = smem + wv * (32 * C::CPR * 16);
+  char* region = row_region<D>(smem, wv);
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     const int row = w.qrow + 32 * qb;
     const int row0 = w.qw0 + 32 * qb;
     const float l_tot = xlane_sum(w.l_run[qb]);
-    store_o_rows<D, T>(region, w.oacc[qb], 1.0f / l_tot, p.o + qoff + (size_t)row0 * D, N - row0, lane);
+    store_rows<D, T>(region, w.oacc[qb], 1.0f / l_tot, p.o + qoff + (size_t)row0 * D, N - row0, lane);
     if (p.lse != nullptr && w.g == 0 && row < N)
       p.lse[((size_t)b * p.Hq + hq) * N + row] = (w.m_run[qb] + __builtin_log2f(l_tot)) * kLn2;
   }

@@ -531,43 +531,52 @@ __device__ __forceinline__ void pv_tile(const char* vs, const PTile<D>& pf, cons
     }
 }
 
-// Stores one wave's 32 finished output rows, O = O^T / l rounded to T.  In
-// the accumulator layout a lane holds 8-byte pieces of its own row at 4 D/32
-// places, so a direct store writes 32 rows x 16 bytes per instruction.  The
-// rows are instead written to the wave's own LDS region (16-byte chunks
-// XOR-swizzled by row, so that neither access pattern meets bank conflicts)
-// and read back so that each lane stores 16 consecutive bytes of a row: the
-// wave's 32 rows are one contiguous range of memory, written in D/16 fully
-// coalesced stores.  `region` (32 * CPR * 16 bytes) must no longer be in use
-// by the K/V copies or reads; rows at or past `rows_valid` are not stored.
-template <int D, typename T>
-__device__ __forceinline__ void store_o_rows(char* region, const f32x16 (&oacc)[Cfg<D>::DT], float inv,
-                                             _Float16* out, int rows_valid, int lane) {
+// Stores one wave's 32 finished rows of an output, acc * mult rounded to T:
+// NDT 32-dim tiles of each row (the dims from `out` on; rows D elements
+// apart in memory).  In the accumulator layout a lane holds 8-byte pieces of
+// its own row (lane % 32) at 4 NDT places, so a direct store writes 32 rows x
+// 16 bytes per instruction.  The rows are instead written to the wave's own
+// LDS region (16-byte chunks XOR-swizzled by row, so that neither access
+// pattern meets bank conflicts) and read back so that each lane stores 16
+// consecutive bytes of a row: fully coalesced stores, 2 NDT of them.
+// `region` (32 * CPR * 16 bytes) must no longer be in use by copies or
+// reads; rows at or past `rows_valid` are not stored.
+template <int D, typename T, int NDT = Cfg<D>::DT>
+__device__ __forceinline__ void store_rows(char* region, const f32x16 (&acc)[NDT], float mult, _Float16* out,
+                                           int rows_valid, int lane) {
   using C = Cfg<D>;
-  constexpr int CH = D / 8;  // 16-byte chunks of a row in memory
+  constexpr int CH = 4 * NDT;  // 16-byte chunks of a row to store
   constexpr int MASK = C::CPR - 1;
+  static_assert(CH <= C::CPR, "a row must fit the LDS row pitch");
   const int r = lane & 31, g = lane >> 5;
   // The region may still be read by this wave's previous call.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       half4 h;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = to_elem<T>(oacc[dt][4 * rq + i] * inv);
+      for (int i = 0; i < 4; ++i) h[i] = to_elem<T>(acc[dt][4 * rq + i] * mult);
       const int c = 4 * dt + rq;  // chunk of dims 32 dt + 8 rq .. +7; this lane's half is 4 g .. 4 g + 3
       *reinterpret_cast<half4*>(region + (r * C::CPR + (c ^ (r & MASK))) * 16 + 8 * g) = h;
     }
   // Every lane's writes land before any lane reads (LDS work of one wave).
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-  for (int it = 0; it < D / 16; ++it) {  // 32 rows x CH chunks over 64 lanes
+  for (int it = 0; it < 2 * NDT; ++it) {  // 32 rows x CH chunks over 64 lanes
     const int p = it * 64 + lane;
     const int row = p / CH, c = p - row * CH;
     const u32x4 x = *reinterpret_cast<const u32x4*>(region + (row * C::CPR + (c ^ (row & MASK))) * 16);
     if (row < rows_valid) *reinterpret_cast<u32x4*>(out + (size_t)row * D + 8 * c) = x;
   }
+}
+
+// LDS region of wave wv for store_rows, inside the K/V stages.
+template <int D>
+__device__ __forceinline__ char* row_region(char* smem, int wv) {
+  static_assert(kWaves * 32 * Cfg<D>::CPR * 16 <= 4 * Cfg<D>::TILE_BYTES, "output staging must fit the K/V stages");
+  return smem + wv * (32 * Cfg<D>::CPR * 16);
 }
 
 // Per-wave state of the software pipeline.
