@@ -3,6 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 
+Without --warmup the warm-up runs for 0.3 s of steps (the GPU clock ramps up
+over the first ~40 ms of load), without --steps about 0.25 s of steps are
+timed; the JSON line reports the counts used.
+
 A step is one call of the whole hot path (one fused forward kernel) over one
 batch of synthetic fp16 inputs already resident in device memory.  The default
 workload is the LLaMA-7B layer shape (B=2, H=32, N=2048, d=128, non-causal),
@@ -52,6 +56,59 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_traffic.json")
 BACKWARD_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_bwd_kernel.hip"]
 BACKWARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_traffic.json")
+
+
+# Without --warmup, warm-up steps run until WARMUP_S seconds have passed: the
+# MI355X clock ramps up over the first ~40 ms of load after idle (a forward
+# step of the LLaMA-7B layer shape takes 266 us in its first 20 steps, 145 us
+# after 20 ms and 138 us from ~60 ms on), so a few steps would time the ramp,
+# not the kernel.  Without --steps, the timed region is about TIMED_S seconds
+# of steps (at least 5).
+WARMUP_S = 0.3
+TIMED_S = 0.25
+
+
+def run_timed(step, args, dev):
+    """Runs the warm-up and the timed steps of `step(i)`; sets args.warmup
+    and args.steps to the counts used and returns (wall ms per step, mean
+    step ms from one pair of HIP events on the launch stream)."""
+    import torch
+
+    if args.warmup is not None:
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        per_step = None
+    else:
+        n, t_start = 0, time.perf_counter()
+        while True:
+            t_batch = time.perf_counter()
+            for _ in range(10):
+                step(n)
+                n += 1
+            torch.cuda.synchronize()
+            now = time.perf_counter()
+            per_step = (now - t_batch) / 10
+            if now - t_start >= WARMUP_S:
+                break
+        args.warmup = n
+    if args.steps is None:
+        args.steps = 50 if per_step is None else max(5, min(5000, int(round(TIMED_S / per_step))))
+    # One pair of HIP events on the launch stream brackets the timed region
+    # (per-step events would add their own timestamp writes to every step);
+    # the kernel's average duration is the region's time over the steps.
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / args.steps, ev0.elapsed_time(ev1) / args.steps
 
 
 def kernel_source_hash(sources=FORWARD_SOURCES) -> str:
@@ -224,22 +281,7 @@ def run_decode(args) -> int:
         kc, vc = kvs[i % copies]
         ea.attn_decode(q, kc, vc, scale=w.scale, causal=w.causal, out=o, lse=lse, workspace=ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    avg_step_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step, avg_step_ms = run_timed(step, args, dev)
     value = w.hbm_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = w.hbm_bytes / (avg_step_ms * 1e-3) / 1e9
     result = {
@@ -350,25 +392,10 @@ def run_backward(args) -> int:
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(max(1, ea.attn_bwd_workspace_size(w.B, w.Hq, w.N, w.d)), dtype=torch.uint8, device=dev)
 
-    def step():
+    def step(_i):
         ea.attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    avg_step_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step, avg_step_ms = run_timed(step, args, dev)
     flops = 10 * w.d * w.pairs
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_step_ms * 1e-3) / 1e12
@@ -413,8 +440,10 @@ def run_backward(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: about %.2f s of them)" % TIMED_S)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: as many as run in %.1f s)" % WARMUP_S)
     ap.add_argument("--workload", type=int, default=2, help="named workload id (1-5)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
@@ -465,29 +494,10 @@ def main() -> int:
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
 
-    def step():
+    def step(_i):
         ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # One pair of HIP events on the launch stream brackets the timed region
-    # (per-step events would add their own timestamp writes to every step);
-    # the kernel's average duration is the region's time over the steps.
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    avg_kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step, avg_kernel_ms = run_timed(step, args, dev)
 
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (avg_kernel_ms * 1e-3) / 1e12
