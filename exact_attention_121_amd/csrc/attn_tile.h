@@ -536,9 +536,10 @@ __device__ __forceinline__ void pv_tile(const char* vs, const PTile<D>& pf, cons
 // apart in memory).  In the accumulator layout a lane holds 8-byte pieces of
 // its own row (lane % 32) at 4 NDT places, so a direct store writes 32 rows x
 // 16 bytes per instruction.  The rows are instead written to the wave's own
-// LDS region (16-byte chunks XOR-swizzled by row, so that neither access
-// pattern meets bank conflicts) and read back so that each lane stores 16
-// consecutive bytes of a row: fully coalesced stores, 2 NDT of them.
+// LDS region (16-byte chunks XOR-swizzled by row: at most 2-way bank
+// conflicts, 4-way for 128-byte rows, once per workgroup) and read back so
+// that each lane stores 16 consecutive bytes of a row: fully coalesced
+// stores, 2 NDT of them.
 // `region` (32 * CPR * 16 bytes) must no longer be in use by copies or
 // reads; rows at or past `rows_valid` are not stored.
 template <int D, typename T, int NDT = Cfg<D>::DT>

@@ -1,0 +1,197 @@
+"""CPU checks of the LDS layout arithmetic the kernels rely on.
+
+The kernels in exact_attention_121_amd/csrc/attn_tile.h place 16-byte chunks
+of each K/V tile row at a position XOR-swizzled by the row's low bits, read
+matrix operands from it, and stage output rows through LDS before storing
+them.  These tests restate that index arithmetic in Python (the swizzle maps
+are read from the header itself) and check, for every supported head_dim,
+the properties the kernels depend on: every map permutes a row's chunks, the
+matrix-operand reads meet no bank conflicts, the output-staging reads find
+exactly what the staging writes put there inside the wave's region (with at
+most the bank conflicts stated there), and the two register-saving
+identities of the copy and transpose-read offsets hold.
+
+Bank model: 4-byte banks, a wavefront's access served 128 or 256 bytes per
+clock (32 or 64 banks), lanes in order; an access is conflict-free when the
+lanes served together touch distinct banks (or the same 4 bytes).
+"""
+
+import os
+import re
+
+import pytest
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "exact_attention_121_amd", "csrc", "attn_tile.h")
+HEAD_DIMS = list(range(32, 257, 32))
+
+
+def _maps():
+    text = open(HEADER).read()
+    m16 = int(re.search(r"kMap16 = (0x[0-9a-f]+)ull", text).group(1), 16)
+    m8 = int(re.search(r"kMap8 = (0x[0-9a-f]+)ull", text).group(1), 16)
+    return m16, m8
+
+
+MAP16, MAP8 = _maps()
+
+
+def cpr(d):
+    """16-byte chunks per (padded) LDS tile row."""
+    return 8 if d <= 64 else (16 if d <= 128 else 32)
+
+
+def key_tile(d):
+    return 32 if d > 128 else 64
+
+
+def f(d, r):
+    m = MAP16 if cpr(d) >= 16 else MAP8
+    return (m >> (4 * (r & 15))) & 15
+
+
+def swz(d, r, c):
+    """Byte offset of chunk c of row r in a swizzled tile."""
+    return (r * cpr(d) + (c ^ f(d, r))) * 16
+
+
+def conflict_degree(addrs_by_lane, nbytes, banks):
+    """addrs_by_lane: the byte address of each lane's access of nbytes; the
+    lanes are served in groups covering banks*4 bytes.  Returns the largest
+    number of distinct 4-byte words one bank must deliver to one group."""
+    per_group = banks * 4 // nbytes
+    worst = 1
+    for g0 in range(0, len(addrs_by_lane), per_group):
+        words = {}
+        for a in addrs_by_lane[g0:g0 + per_group]:
+            for w in range(a // 4, (a + nbytes) // 4):
+                words.setdefault(w % banks, set()).add(w)
+        worst = max(worst, max(len(v) for v in words.values()))
+    return worst
+
+
+def conflict_free(addrs_by_lane, nbytes, banks):
+    return conflict_degree(addrs_by_lane, nbytes, banks) == 1
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_swizzle_permutes_each_row(d):
+    c = cpr(d)
+    for r in range(key_tile(d)):
+        got = sorted(swz(d, r, ch) for ch in range(c))
+        assert got == [(r * c + ch) * 16 for ch in range(c)]
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_k_operand_reads_conflict_free(d):
+    # ds_read_b128 of a K operand: lane L reads row 32 t + L % 32 at chunk
+    # 2 dc + L / 32 (dims 16 dc + 8 (L / 32) .. + 7).
+    for banks in (32, 64):
+        for t in range(key_tile(d) // 32):
+            for dc in range(d // 16):
+                addrs = [swz(d, 32 * t + (L & 31), 2 * dc + (L >> 5)) for L in range(64)]
+                assert conflict_free(addrs, 16, banks), (d, banks, t, dc)
+
+
+def v_read_offset(d, lane, hi, dt):
+    """Transpose read of V (ds_read_b64_tr_b16): the lane's key row and dims
+    inside row tile dt, as Offsets::init computes them."""
+    g, m16 = lane >> 5, lane & 15
+    dsub = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3)
+    dim = 32 * dt + dsub
+    return swz(d, 4 * g + (m16 >> 2) + 8 * hi, dim >> 3) + (dim & 7) * 2
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_v_transpose_reads_conflict_free(d):
+    for banks in (32, 64):
+        for hi in (0, 1):
+            for dt in range(d // 32):
+                for kb in range(0, key_tile(d), 16):  # key groups 16 h + 32 t
+                    addrs = [v_read_offset(d, L, hi, dt) + kb * cpr(d) * 16 for L in range(64)]
+                    assert conflict_free(addrs, 8, banks), (d, banks, hi, dt, kb)
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_group1_reads_from_group0_identity(d):
+    # With the 16-entry map, row r + 8 XORs with f(r) ^ 8: the transposed
+    # reads of key group 1 in row tile dt are those of group 0 in row tile
+    # dt ^ 2, eight rows on (used when the row tiles come in fours).
+    c = cpr(d)
+    vr = 4 if (c == 32 and d // 32 > 4) else d // 32
+    if not (c >= 16 and vr % 4 == 0):
+        pytest.skip("identity not used at this head_dim")
+    for r in range(8):
+        assert f(d, r + 8) == f(d, r) ^ 8
+    for lane in range(64):
+        for dt in range(vr):
+            assert v_read_offset(d, lane, 1, dt) == v_read_offset(d, lane, 0, dt ^ 2) + 8 * c * 16
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_copy_offsets_repeat_every_period(d):
+    # LoadOffsets keeps kPeriod offsets: load i of a thread covers tile row
+    # (i * 256 + tid) / CPR, and its chunk's swizzled slot repeats, a whole
+    # number of rows further on, every kPeriod loads.
+    c = cpr(d)
+    rows_per_load = 256 // c
+    period = 1 if rows_per_load >= 16 else 16 // rows_per_load
+    loads = key_tile(d) * c // 256
+    for tid in range(256):
+        def src_chunk(i):
+            p = i * 256 + tid
+            row = p // c
+            return row, (swz(d, row, p % c) >> 4) - row * c
+        for i in range(loads):
+            r0, c0 = src_chunk(i % period)
+            r1, c1 = src_chunk(i)
+            assert c1 == c0 and r1 - r0 == (i // period) * period * rows_per_load
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_output_staging_round_trip(d):
+    # store_rows: lane (r = L % 32, g = L / 32) writes 8 bytes of dims
+    # 32 dt + 8 rq + 4 g .. + 3 of row r at chunk c = 4 dt + rq, swizzled by
+    # r & (CPR - 1); then lane L of step it reads the 16-byte chunk
+    # p % CH of row p / CH (p = 64 it + L) for a row-contiguous store.
+    # Bank conflicts, which cost a few cycles once per workgroup: the reads
+    # are conflict-free when a row's chunks fill whole groups of lanes
+    # (head_dims 64, 128, 256) and at most 2-way where a group straddles two
+    # rows; the writes put rows r and r + 16 (r and r + 8 in 128-byte rows)
+    # on the same banks, 2- to 4-way.
+    c = cpr(d)
+    mask = c - 1
+    region = 32 * c * 16
+    written = {}
+    for dt in range(d // 32):
+        for rq in range(4):
+            ch = 4 * dt + rq
+            addrs = []
+            for lane in range(64):
+                r, g = lane & 31, lane >> 5
+                a = (r * c + (ch ^ (r & mask))) * 16 + 8 * g
+                addrs.append(a)
+                assert 0 <= a and a + 8 <= region
+                for k in range(4):
+                    written[a + 2 * k] = (r, 32 * dt + 8 * rq + 4 * g + k)
+            for banks in (32, 64):
+                assert conflict_degree(addrs, 8, banks) <= (4 if c == 8 else 2)
+    assert len(written) == 32 * d  # every (row, dim) once
+    chunks = d // 8
+    stores = set()
+    for it in range(d // 16):
+        addrs = []
+        for lane in range(64):
+            p = it * 64 + lane
+            row, ch = p // chunks, p % chunks
+            a = (row * c + (ch ^ (row & mask))) * 16
+            addrs.append(a)
+            for k in range(8):  # the 8 elements this lane stores to dims 8 ch .. 8 ch + 7 of its row
+                assert written[a + 2 * k] == (row, 8 * ch + k)
+            stores.add((row, ch))
+        for banks in (32, 64):
+            limit = 1 if d in (64, 128, 256) else 2
+            assert conflict_degree(addrs, 16, banks) <= limit, (d, it, banks)
+    assert len(stores) == 32 * chunks
+    # the four waves' regions fit the K/V stages (4 tiles of key_tile rows)
+    assert 4 * region <= 4 * key_tile(d) * c * 16
