@@ -172,9 +172,13 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
   // Iteration 0 refills K stage 0: every wave must be done reading K_0.
   __syncthreads();
 
+  // Without the mask every wave could compute every tile (a wave entirely
+  // past the end only computes rows that are never stored); at d = 64 the
+  // pipeline is scheduled better when it is told so.
+  constexpr bool kUniform = !CAUSAL && D == 64;
   for (int j = 0; j < nt; j += 2) {
-    pipeline_step<D, CAUSAL, 0, T>(j, nt, smem, krs, vrs, lo, tid, w, sa, sb);
-    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1, T>(j + 1, nt, smem, krs, vrs, lo, tid, w, sb, sa);
+    pipeline_step<D, CAUSAL, 0, T, kUniform>(j, nt, smem, krs, vrs, lo, tid, w, sa, sb);
+    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1, T, kUniform>(j + 1, nt, smem, krs, vrs, lo, tid, w, sb, sa);
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).  After the loop's last
