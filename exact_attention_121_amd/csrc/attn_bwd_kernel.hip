@@ -71,6 +71,7 @@ struct BwdParams {
   int N, Npad, Hq, Hkv, group, rows_total;
   float c;            // scale * log2(e), any sign
   float scale;
+  int group_dkdv, group_dq;   // causal: heads whose tiles run interleaved, heaviest first
 };
 
 // ---------------------------------------------------------------------------
@@ -105,16 +106,6 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(BwdParams p) {
     p.delta[row] = acc;
     p.lse2[row] = i < p.N ? p.lse[(size_t)bh * p.N + i] * kLog2e : INFINITY;
   }
-}
-
-// Workgroup id -> work index, so that each of the 8 XCDs (one L2 each)
-// receives a contiguous range of work: the tiles of one head then share the
-// operands they all re-read in one L2 (consecutive ids go round-robin over
-// the XCDs).
-__device__ __forceinline__ int xcd_work_index() {
-  const int nb = gridDim.x, bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3, q8 = nb >> 3, r8 = nb & 7;
-  return xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
 }
 
 // Probabilities and dS of one tile from the scores s and dP, with per-entry
@@ -234,10 +225,21 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
 
   constexpr int NP = bwd_dim_parts<D>();
   constexpr int NDT = C::DT / NP;       // 32-dim output tiles of this workgroup
+  // Work list position -> (K/V head, key tile, dim part), contiguous per
+  // XCD; causal: the heaviest key tiles (the first) first across a group of
+  // heads.
   const int wi = xcd_work_index();
-  const int part = wi % NP;
-  const int kt = (wi / NP) % k_tiles;
-  const int bk = wi / NP / k_tiles;   // b * Hkv + kvh
+  int part, kt, bk;   // bk = b * Hkv + kvh
+  if (CAUSAL) {
+    int rank;
+    grouped_order(wi, k_tiles * NP, gridDim.x / (k_tiles * NP), p.group_dkdv, bk, rank);
+    part = rank % NP;
+    kt = rank / NP;
+  } else {
+    part = wi % NP;
+    kt = (wi / NP) % k_tiles;
+    bk = wi / NP / k_tiles;
+  }
   const int b = bk / p.Hkv, kvh = bk - b * p.Hkv;
   const int N = p.N;
   const int k0 = kt * kBwdKeys;
@@ -430,10 +432,17 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
   static_assert(C::QB == 1, "one 32-row block per wave");
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
 
+  // As in the forward: causal query tiles heaviest first across a group of
+  // heads.
   const int wi = xcd_work_index();
-  int qt = wi % q_tiles;
-  const int bh = wi / q_tiles;   // b * Hq + hq
-  if (CAUSAL) qt = q_tiles - 1 - qt;     // heaviest tiles first
+  int qt, bh;   // bh = b * Hq + hq
+  if (CAUSAL) {
+    grouped_order(wi, q_tiles, gridDim.x / q_tiles, p.group_dq, bh, qt);
+    qt = q_tiles - 1 - qt;
+  } else {
+    qt = wi % q_tiles;
+    bh = wi / q_tiles;
+  }
   const int b = bh / p.Hq, hq = bh - b * p.Hq, kvh = hq / p.group;
   const int N = p.N;
   const int q0 = qt * C::BM;
@@ -529,8 +538,19 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
 }
 
 template <int D, bool CAUSAL, typename T>
-hipError_t launch_bwd_t(const BwdArgs& a, const BwdParams& p, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdArgs& a, BwdParams p, hipStream_t s) {
   using C = Cfg<D>;
+  // Work order groups (causal): a dK/dV head streams the Q and dO of its
+  // query heads, a dQ head its K/V head (16-bit elements).
+  {
+    const int64_t k_tiles = (a.N + kBwdKeys - 1) / kBwdKeys;
+    const int64_t units = k_tiles * bwd_dim_parts<D>();
+    p.group_dkdv = CAUSAL ? causal_head_group(static_cast<int64_t>(a.B) * a.Hkv * units, units,
+                                              static_cast<int64_t>(p.group) * a.N * D * 4, 1) : 1;
+    const int64_t q_tiles = (a.N + C::BM - 1) / C::BM;
+    p.group_dq = CAUSAL ? causal_head_group(static_cast<int64_t>(a.B) * a.Hq * q_tiles, q_tiles,
+                                            static_cast<int64_t>(a.N) * D * 4, p.group) : 1;
+  }
   constexpr int rows_per_wg = kThreads / prep_lanes<D>();
   const unsigned prep_grid = static_cast<unsigned>((p.rows_total + rows_per_wg - 1) / rows_per_wg);
   hipLaunchKernelGGL((attn_bwd_prep_kernel<D, T>), dim3(prep_grid), dim3(kThreads), 0, s, p);

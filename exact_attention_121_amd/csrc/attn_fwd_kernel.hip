@@ -76,7 +76,7 @@ struct Params {
   _Float16* o;
   float* lse;
   int N, Hq, Hkv, group, q_tiles;
-  int head_group;   // causal: heads whose query tiles are interleaved heaviest first
+  int head_group;   // causal: heads whose query tiles run interleaved, heaviest first
   float c;          // |scale| * log2(e), or 1 when scale = 0 (Q is then zeroed): always > 0
   uint32_t q_sign;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
   uint32_t q_keep;  // 0 when scale = 0 (every logit is then exactly 0), else all ones
@@ -88,23 +88,13 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
   // K stages 0/1 then V stages 0/1.
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
 
-  // Workgroup id -> (batch*head, query tile), contiguous per XCD.
-  const int nb = gridDim.x, bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3, q8 = nb >> 3, r8 = nb & 7;
-  const int u = xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+  // Work list position -> (batch*head, query tile), contiguous per XCD;
+  // causal: heaviest tiles first across a group of heads.
+  const int u = xcd_work_index();
   int bh, qt;
   if (CAUSAL) {
-    // Heads go in groups of head_group; inside a group the query tiles of
-    // all its heads run heaviest first (the last tile of every head, then
-    // the one before it, ...), so that the light tiles fill the tail.
-    const int per_group = p.head_group * p.q_tiles;
-    const int hg = u / per_group;
-    const int rem = u - hg * per_group;
-    const int bh_total = gridDim.x / p.q_tiles;
-    const int in_group = min(p.head_group, bh_total - hg * p.head_group);
-    const int rank = rem / in_group;
-    bh = hg * p.head_group + (rem - rank * in_group);
-    qt = p.q_tiles - 1 - rank;
+    grouped_order(u, p.q_tiles, gridDim.x / p.q_tiles, p.head_group, bh, qt);
+    qt = p.q_tiles - 1 - qt;
   } else {
     bh = u / p.q_tiles;
     qt = u - bh * p.q_tiles;
@@ -211,37 +201,12 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
   }
 }
 
-// Causal work order: how many heads interleave their query tiles heaviest
-// first.  A group never straddles two XCDs' ranges of work (the ranges must
-// hold whole heads, else 1), and its distinct K/V heads fit kHeadGroupBytes
-// of L2 (at least one K/V head, however large): measured on gfx950, 8 heads
-// of the spiky causal prefill (1 MB of K/V each) run 8 % faster than one at
-// a time, 4 query heads of one 8 MB GQA K/V head 3 %, while groups that
-// straddle XCDs or hold 16 MB of K/V lose 20-30 %.  ATTN_HEADGROUP (the
-// tile sweep's hook) fixes the group size instead.
-constexpr int64_t kHeadGroupBytes = 8 << 20;
-
-inline int causal_head_group(unsigned grid, int q_tiles, int N, int d, int group) {
-#ifdef ATTN_HEADGROUP
-  if (ATTN_HEADGROUP > 0) return ATTN_HEADGROUP <= static_cast<int>(grid / q_tiles) ? ATTN_HEADGROUP : 1;
-#endif
-  if (grid % 8 != 0 || (grid / 8) % q_tiles != 0) return 1;
-  const int64_t per_xcd = grid / 8 / q_tiles;                    // whole heads per XCD
-  const int64_t kv_bytes = static_cast<int64_t>(N) * d * 2 * 2;  // K and V of one head, 16-bit elements
-  int64_t kv_fit = kHeadGroupBytes / kv_bytes;
-  if (kv_fit < 1) kv_fit = 1;
-  const int64_t cap = kv_fit * group;  // query heads that share those K/V heads
-  int64_t g = 1;
-  for (int64_t c = 1; c <= per_xcd && c <= cap; ++c)
-    if (per_xcd % c == 0) g = c;
-  return static_cast<int>(g);
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch_t(const LaunchArgs& a, Params p, hipStream_t s) {
   p.q_tiles = (a.N + Cfg<D>::BM - 1) / Cfg<D>::BM;
   const unsigned grid = static_cast<unsigned>(a.B) * a.Hq * p.q_tiles;
-  p.head_group = CAUSAL ? causal_head_group(grid, p.q_tiles, a.N, D, a.Hq / a.Hkv) : 1;
+  // Each head streams its K/V head (K and V, 16-bit elements) through L2.
+  p.head_group = CAUSAL ? causal_head_group(grid, p.q_tiles, static_cast<int64_t>(a.N) * D * 4, a.Hq / a.Hkv) : 1;
   if (a.bf16)
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, __bf16>), dim3(grid), dim3(kThreads), 0, s, p);
   else

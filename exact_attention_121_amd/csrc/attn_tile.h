@@ -591,6 +591,30 @@ struct WaveState {
   int N, qw0, qrow, g, nt_w;  // qrow: row of this lane in block 0; nt_w: key tiles this wave computes
 };
 
+// Workgroup id -> position in the list of work, so that each of the 8 XCDs
+// (one L2 each) receives a contiguous range of it (consecutive ids go
+// round-robin over the XCDs).
+__device__ __forceinline__ int xcd_work_index() {
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3, q8 = nb >> 3, r8 = nb & 7;
+  return xcd * q8 + (xcd < r8 ? xcd : r8) + slot;
+}
+
+// Causal work order: position u of the list -> (head, rank), rank 0 the
+// heaviest of the head's `units` tiles.  Heads go in groups of `group`
+// (causal_head_group in attn_launch.h); inside a group the tiles of all its
+// heads run heaviest first (rank 0 of every head, then rank 1, ...), so that
+// the light tiles of the last heads fill the tail.  A bijection for any
+// group size (the last group may be smaller).
+__device__ __forceinline__ void grouped_order(int u, int units, int heads, int group, int& head, int& rank) {
+  const int per_group = group * units;
+  const int hg = u / per_group;
+  const int rem = u - hg * per_group;
+  const int in_group = min(group, heads - hg * group);
+  rank = rem / in_group;
+  head = hg * group + (rem - rank * in_group);
+}
+
 // LDS layout: K tiles in stages 0/1, then V tiles in stages 0/1.
 template <int D>
 __device__ __forceinline__ char* k_stage(char* smem, int st) { return smem + st * Cfg<D>::TILE_BYTES; }
