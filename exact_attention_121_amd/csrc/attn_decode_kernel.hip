@@ -39,8 +39,8 @@ struct DecParams {
   uint32_t q_sign, q_keep;
 };
 
-template <int D, bool CAUSAL, typename T>
-__global__ __launch_bounds__(kThreads, Cfg<D>::WG_PER_CU) void attn_decode_split_kernel(DecParams p) {
+template <int D, bool CAUSAL, typename T, int WGS>
+__global__ __launch_bounds__(kThreads, WGS) void attn_decode_split_kernel(DecParams p) {
   using C = Cfg<D>;
   static_assert(C::QB == 1 && C::BM == kDecodeRows, "decode packs 128 rows per workgroup, 32 per wave");
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
@@ -267,10 +267,14 @@ __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(MergeP
 template <int D, bool CAUSAL, typename T>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecParams& dp, const MergeParams& mp, hipStream_t s) {
   static_assert(Cfg<D>::BN == decode_key_tile(D), "the decode plan and the kernel must use the same key tile");
-  static_assert(Cfg<D>::WG_PER_CU * 256 == decode_target_groups(D), "the split plan must fill the chip once");
   const unsigned groups = static_cast<unsigned>(a.B) * a.Hkv * static_cast<unsigned>(a.plan.row_blocks);
-  hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL, T>), dim3(groups * static_cast<unsigned>(a.plan.splits)),
-                     dim3(kThreads), 0, s, dp);
+  const unsigned grid = groups * static_cast<unsigned>(a.plan.splits);
+  constexpr int kWide = D == 256 ? 2 : static_cast<int>(default_wg_per_cu(D));
+  if (decode_wg_per_cu(D, grid) == kWide)
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL, T, kWide>), dim3(grid), dim3(kThreads), 0, s, dp);
+  else
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, CAUSAL, T, static_cast<int>(default_wg_per_cu(D))>), dim3(grid),
+                       dim3(kThreads), 0, s, dp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.splits == 1) return e;
   const unsigned rows = static_cast<unsigned>(a.B) * a.Hq * a.Nq;

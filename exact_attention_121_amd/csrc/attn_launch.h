@@ -71,6 +71,15 @@ constexpr int64_t default_wg_per_cu(int64_t d) { return d <= 224 ? 2 : 1; }
 // the split count aims at one full round of them.
 constexpr int64_t decode_target_groups(int64_t d) { return 256 * default_wg_per_cu(d); }
 
+// Workgroups per CU of the decode kernel, chosen at launch: the default
+// build's count, except that at d = 256 a grid of at least two workgroups
+// per CU runs a second instance compiled for two (it spills 72 bytes per
+// lane and still streams a batch of long caches 7 % faster; on a grid of one
+// workgroup per CU the spilling instance is 18 % slower).
+constexpr int64_t decode_wg_per_cu(int64_t d, int64_t grid) {
+  return d == 256 && grid >= 512 ? 2 : default_wg_per_cu(d);
+}
+
 struct DecodePlan {
   int64_t row_blocks, kv_tiles, splits, chunk_tiles;
   int64_t workspace_bytes;  // partial O (fp32) and LSE (fp32) of every split

@@ -64,7 +64,7 @@ EDGE = [
     (1, 4, 4, 5, 5),
     (1, 2, 1, 1, 4097),
     (2, 8, 8, 2, 33),
-    (64, 8, 8, 1, 200),      # 512 row blocks: one split, no merge, several key tiles
+    (64, 8, 8, 1, 200),      # 512 row blocks: one split, no merge, several key tiles; d = 256: the two-per-CU instance
 ]
 
 
