@@ -62,7 +62,8 @@
 //   * Workgroup ids are remapped so that each of the 8 XCDs (each with its
 //     own L2) receives a contiguous range of (head, query tile) work, i.e. the
 //     query tiles of the same heads share their K/V in one L2; causal query
-//     tiles run heaviest first.
+//     tiles run heaviest first, interleaved across a group of heads so that
+//     the light tiles of the XCD's last heads fill the tail.
 
 #include "attn_tile.h"
 
