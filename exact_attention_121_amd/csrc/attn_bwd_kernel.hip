@@ -126,20 +126,28 @@ __device__ __forceinline__ void p_and_ds(const STile<D>& arg, const STile<D>& dp
     }
 }
 
-// Output dim tiles per dK/dV workgroup: with head_dim 256 the two halves of
-// the dims go to two workgroups (each recomputes S and dP), so that the dK
-// and dV accumulators fit in the register file next to K and V.
+// Workgroups per key block of dK/dV (each takes 1/parts of the output dims
+// and recomputes S and dP), chosen at launch.  One everywhere except d = 256
+// on a grid of fewer than kDkdvOnePartMinGrid key blocks: there the dims are
+// split in two, which doubles the workgroups (and the S / dP work).  With
+// one part, d = 256 keeps K, V and both accumulators in 504 registers (the
+// sub-tile form, no spill; the whole-tile form spills 68 bytes) at one
+// workgroup per CU: +23 % on the LLaMA-7B layer shape and +8.5 % on the
+// causal GQA workload (512 key blocks) on MI355X, but -24 % on a 256-block
+// grid, where the split's second workgroup per block is what fills the CUs.
+constexpr unsigned kDkdvOnePartMinGrid = 512;
 template <int D>
-constexpr int bwd_dim_parts() { return D == 256 ? 2 : 1; }
+inline int bwd_dim_parts(unsigned key_blocks) { return D == 256 && key_blocks < kDkdvOnePartMinGrid ? 2 : 1; }
 
 // Order of the dK/dV work inside a step: one 32-query sub-tile at a time
 // (SUB: fewer live registers, two workgroups per CU up to d = 128) or the
 // whole tile at once (more independent matrix work in flight per wave).
-// Measured on gfx950: sub-tiles are faster without the causal mask, except
-// at d = 256, once the grid gives every CU two workgroups; with the mask,
-// or on smaller grids, the whole tile is.
+// Measured on gfx950: sub-tiles are faster without the causal mask once the
+// grid gives every CU two workgroups (at d = 256 with one dim part: one
+// workgroup per CU either way, and the whole tile would spill); with the
+// mask, or on smaller grids, the whole tile is.
 template <int D, bool CAUSAL>
-constexpr bool bwd_dkdv_subtile_form() { return !CAUSAL && D != 256; }
+constexpr bool bwd_dkdv_subtile_form() { return !CAUSAL; }
 constexpr unsigned kDkdvSubtileMinGrid = 512;   // two workgroups for each of the 256 CUs
 
 // dK/dV workgroups per CU the register budget allows (K, V and the two
@@ -214,7 +222,7 @@ __device__ __forceinline__ void tr_times_p(const char* stage, const half8 (&p)[2
 // dK, dV.  Query tiles of BN rows stream through LDS (Q in the "K" stages,
 // dO in the "V" stages); the wave's 32 keys are the columns of S and dP.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool SUB, typename T>
+template <int D, bool CAUSAL, bool SUB, int NP, typename T>
 __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn_bwd_dkdv_kernel(BwdParams p, int k_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-key block per wave");
@@ -223,7 +231,6 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES + 2 * 2 * 64 * 4];
   float* const rowterms = reinterpret_cast<float*>(smem + 4 * C::TILE_BYTES);  // [stage][lse2 | delta][64]
 
-  constexpr int NP = bwd_dim_parts<D>();
   constexpr int NDT = C::DT / NP;       // 32-dim output tiles of this workgroup
   // Work list position -> (K/V head, key tile, dim part), contiguous per
   // XCD; causal: the heaviest key tiles (the first) first across a group of
@@ -542,9 +549,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, BwdParams p, hipStream_t s) {
   using C = Cfg<D>;
   // Work order groups (causal): a dK/dV head streams the Q and dO of its
   // query heads, a dQ head its K/V head (16-bit elements).
+  const int k_tiles = (a.N + kBwdKeys - 1) / kBwdKeys;
+  const unsigned key_blocks = static_cast<unsigned>(a.B) * a.Hkv * k_tiles;
+  const int parts = bwd_dim_parts<D>(key_blocks);
   {
-    const int64_t k_tiles = (a.N + kBwdKeys - 1) / kBwdKeys;
-    const int64_t units = k_tiles * bwd_dim_parts<D>();
+    const int64_t units = static_cast<int64_t>(k_tiles) * parts;
     p.group_dkdv = CAUSAL ? causal_head_group(static_cast<int64_t>(a.B) * a.Hkv * units, units,
                                               static_cast<int64_t>(p.group) * a.N * D * 4, 1) : 1;
     const int64_t q_tiles = (a.N + C::BM - 1) / C::BM;
@@ -556,13 +565,22 @@ hipError_t launch_bwd_t(const BwdArgs& a, BwdParams p, hipStream_t s) {
   hipLaunchKernelGGL((attn_bwd_prep_kernel<D, T>), dim3(prep_grid), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int k_tiles = (a.N + kBwdKeys - 1) / kBwdKeys;
-  const unsigned dkdv_grid = static_cast<unsigned>(a.B) * a.Hkv * k_tiles * bwd_dim_parts<D>();
-  if (bwd_dkdv_subtile_form<D, CAUSAL>() && dkdv_grid >= kDkdvSubtileMinGrid)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, bwd_dkdv_subtile_form<D, CAUSAL>(), T>), dim3(dkdv_grid),
-                       dim3(kThreads), 0, s, p, k_tiles);
-  else
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, false, T>), dim3(dkdv_grid), dim3(kThreads), 0, s, p, k_tiles);
+  const unsigned dkdv_grid = key_blocks * static_cast<unsigned>(parts);
+  [&] {
+    if constexpr (D == 256) {
+      if (parts == 2) {
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, false, 2, T>), dim3(dkdv_grid), dim3(kThreads), 0, s, p,
+                           k_tiles);
+        return;
+      }
+    }
+    if (bwd_dkdv_subtile_form<D, CAUSAL>() && dkdv_grid >= kDkdvSubtileMinGrid)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, bwd_dkdv_subtile_form<D, CAUSAL>(), 1, T>),
+                         dim3(dkdv_grid), dim3(kThreads), 0, s, p, k_tiles);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, false, 1, T>), dim3(dkdv_grid), dim3(kThreads), 0, s, p,
+                         k_tiles);
+  }();
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int q_tiles = (a.N + C::BM - 1) / C::BM;

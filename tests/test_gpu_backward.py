@@ -155,3 +155,21 @@ def test_backward_subtile_form(d):
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = attention_bwd_ref(q[sl], k[sl], v[sl], do[sl], scale, causal=False)
         assert_grad_parity([x[sl] for x in got], ref, f"sub-tile form d={d} head ({b}, {h})")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_d256_one_dim_part(causal):
+    """d = 256 on a grid of 512 key blocks (B=4, H=16, N=1024), where the
+    dK/dV kernel takes all 256 output dims in one workgroup per key block (the
+    sub-tile form without the mask, the whole tile with it); the oracle checks
+    two whole (batch, head) pairs."""
+    B, H, N, d = 4, 16, 1024, 256
+    _say(f"[bwd] d=256 one dim part B={B} H={H} N={N} causal={causal}")
+    q, k, v = make_qkv(B, H, H, N, d, seed=2560 + int(causal))
+    do = make_dout(q.shape, seed=2570 + int(causal))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = gpu_backward(q, k, v, do, scale, causal)
+    for b, h in [(0, 0), (3, 15)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = attention_bwd_ref(q[sl], k[sl], v[sl], do[sl], scale, causal=causal)
+        assert_grad_parity([x[sl] for x in got], ref, f"d=256 one part causal={causal} head ({b}, {h})")
