@@ -17,7 +17,7 @@ workload, and a parity check of the timed output against that sample.
 
     python bench.py --backward [--workload 2]
 
-times the backward pass instead: a step is one attn_bwd call (three kernels)
+times the backward pass instead: a step is one attn_bwd call (two kernels)
 given the forward's O and LSE; FLOPs are 10 d per visible (query, key) pair
 (the four gradient products and the recomputed scores).
 
@@ -421,9 +421,9 @@ def run_backward(args) -> int:
                      "traffic": None if bf16 else measured_traffic(w.name, BACKWARD_TRAFFIC_FILE, BACKWARD_SOURCES,
                                                                    "hbm_bytes_per_step"),
                      "flops_per_step": flops,
-                     "scope": "whole step: prep, dK/dV and dQ kernels; 10 d FLOPs per visible pair"},
+                     "scope": "whole step: dQ (with the row terms) and dK/dV kernels; 10 d FLOPs per visible pair"},
         "kernel_ms": {"mean": round(avg_step_ms, 5), "timing": "HIP events on the launch stream around "
-                      f"all {args.steps} timed steps (three kernels per step)"},
+                      f"all {args.steps} timed steps (two kernels per step)"},
         "kernel_code_sha256_16": kernel_source_hash(BACKWARD_SOURCES),
     }
     if args.calibrate_copy_mib > 0:

@@ -13,24 +13,25 @@
 //   dQ = scale dS K,  dK = scale dS^T Q
 // As in the forward, S and P never leave the chip.
 //
-// Three kernels:
-//   * attn_bwd_prep_kernel: Delta_i and LSE_i * log2(e) per query row, into a
-//     workspace padded to whole 128-row tiles (padding rows: Delta = 0 and
-//     LSE = +inf, so that their probabilities are exactly 0 with no bounds
-//     check).
-//   * attn_bwd_dkdv_kernel: one workgroup per 128 keys of one key/value head
-//     (32 per wave, the lanes' columns; with head_dim 256, per half of the
-//     output dims as well); K and V stay in registers as matrix
-//     operands; the Q and dO tiles of every query head of the group stream
-//     through LDS.  Per query tile: S = Q K^T and dP = dO V^T on the matrix
-//     cores, P and dS on the vector ALUs, then dV^T += dO^T P and
-//     dK^T += Q^T dS with P and dS used straight from registers and the
-//     transposed tiles read with ds_read_b64_tr_b16 (the forward's P.V step).
-//     Two forms of that step, chosen at launch: the whole tile at once, or
-//     one 32-query half at a time, which keeps fewer registers live and runs
-//     two workgroups per CU (non-causal grids of two workgroups per CU).
+// Two kernels, dQ first:
 //   * attn_bwd_dq_kernel: one workgroup per 128 query rows, shaped like the
 //     forward kernel: S^T = K Q^T and dP^T = V dO^T, then dQ^T += K^T dS^T.
+//     Its prologue also computes each row's Delta_i = dO_i . O_i and
+//     LSE_i * log2(e) and stores them in a workspace padded to whole 128-row
+//     tiles (padding rows: Delta = 0 and LSE = +inf, so that their
+//     probabilities are exactly 0 with no bounds check).
+//   * attn_bwd_dkdv_kernel: one workgroup per 128 keys of one key/value head
+//     (32 per wave, the lanes' columns; with head_dim 256 on small grids, per
+//     half of the output dims as well); K and V stay in registers as matrix
+//     operands; the Q and dO tiles of every query head of the group stream
+//     through LDS with their Delta / LSE rows.  Per query tile: S = Q K^T and
+//     dP = dO V^T on the matrix cores, P and dS on the vector ALUs, then
+//     dV^T += dO^T P and dK^T += Q^T dS with P and dS used straight from
+//     registers and the transposed tiles read with ds_read_b64_tr_b16 (the
+//     forward's P.V step).  Two forms of that step, chosen at launch: the
+//     whole tile at once, or one 32-query half at a time, which keeps fewer
+//     registers live and runs two workgroups per CU (non-causal grids of two
+//     workgroups per CU).
 // The two main kernels recompute S and dP each; there are no atomics, and
 // every output element is written once.
 //
@@ -73,40 +74,6 @@ struct BwdParams {
   float scale;
   int group_dkdv, group_dq;   // causal: heads whose tiles run interleaved, heaviest first
 };
-
-// ---------------------------------------------------------------------------
-// Delta and LSE in log2 units.  A power-of-two group of lanes per row, D / 8
-// of them with a 16-byte load each, the row's partial dot products summed
-// with lane shuffles.
-// ---------------------------------------------------------------------------
-template <int D>
-constexpr int prep_lanes() { return D <= 32 ? 4 : (D <= 64 ? 8 : (D <= 128 ? 16 : 32)); }
-
-template <int D, typename T>
-__global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(BwdParams p) {
-  constexpr int CH = prep_lanes<D>();       // lanes per row
-  constexpr int ROWS = kThreads / CH;       // rows per workgroup
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x * ROWS + tid / CH;   // (b * Hq + hq) * Npad + i
-  const int part = tid % CH;
-  if (row >= p.rows_total) return;          // whole lane groups leave together
-  const int bh = row / p.Npad;
-  const int i = row - bh * p.Npad;
-  float acc = 0.f;
-  if (i < p.N && part < D / 8) {
-    const size_t off = ((size_t)bh * p.N + i) * D + part * 8;
-    const half8 a = *reinterpret_cast<const half8*>(p.o + off);
-    const half8 g = *reinterpret_cast<const half8*>(p.dout + off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += from_elem<T>(a[e]) * from_elem<T>(g[e]);
-  }
-#pragma unroll
-  for (int w = CH / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
-  if (part == 0) {
-    p.delta[row] = acc;
-    p.lse2[row] = i < p.N ? p.lse[(size_t)bh * p.N + i] * kLog2e : INFINITY;
-  }
-}
 
 // Probabilities and dS of one tile from the scores s and dP, with per-entry
 // LSE (log2) and Delta: P = exp2(c s - lse2), masked entries (arg = -inf)
@@ -462,14 +429,25 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
 
   const size_t qoff = (size_t)bh * N * D;
   QFrag<D> qf, df;
+  float dpart = 0.f;   // this lane's half of Delta = dO . O for its row
 #pragma unroll
   for (int dc = 0; dc < C::DC; ++dc) {
     const size_t e = qoff + (size_t)row * D + 16 * dc + 8 * g;
     qf[0][dc] = row < N ? *reinterpret_cast<const half8*>(p.q + e) : half8{};
     df[0][dc] = row < N ? *reinterpret_cast<const half8*>(p.dout + e) : half8{};
+    const half8 of = row < N ? *reinterpret_cast<const half8*>(p.o + e) : half8{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dpart += from_elem<T>(df[0][dc][i]) * from_elem<T>(of[i]);
   }
-  const float lse2 = p.lse2[(size_t)bh * p.Npad + row];   // +inf past N
-  const float delta = p.delta[(size_t)bh * p.Npad + row];
+  // The row terms: Delta (the other half from lane L ^ 32) and LSE in log2
+  // units, +inf and 0 past N (probabilities exactly 0).  Stored for the
+  // dK/dV kernel, which runs after this one.
+  const float delta = xlane_sum(dpart);
+  const float lse2 = row < N ? p.lse[(size_t)bh * N + row] * kLog2e : INFINITY;
+  if (g == 0) {
+    p.delta[(size_t)bh * p.Npad + row] = delta;
+    p.lse2[(size_t)bh * p.Npad + row] = lse2;
+  }
   OAcc<D> dq_acc;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) dq_acc[0][dt] = f32x16{};
@@ -560,9 +538,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, BwdParams p, hipStream_t s) {
     p.group_dq = CAUSAL ? causal_head_group(static_cast<int64_t>(a.B) * a.Hq * q_tiles, q_tiles,
                                             static_cast<int64_t>(a.N) * D * 4, p.group) : 1;
   }
-  constexpr int rows_per_wg = kThreads / prep_lanes<D>();
-  const unsigned prep_grid = static_cast<unsigned>((p.rows_total + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((attn_bwd_prep_kernel<D, T>), dim3(prep_grid), dim3(kThreads), 0, s, p);
+  // dQ first: it also writes the per-row Delta and LSE terms the dK/dV
+  // kernel reads.
+  const int q_tiles = (a.N + C::BM - 1) / C::BM;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, T>), dim3(static_cast<unsigned>(a.B) * a.Hq * q_tiles),
+                     dim3(kThreads), 0, s, p, q_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned dkdv_grid = key_blocks * static_cast<unsigned>(parts);
@@ -581,11 +561,6 @@ hipError_t launch_bwd_t(const BwdArgs& a, BwdParams p, hipStream_t s) {
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, false, 1, T>), dim3(dkdv_grid), dim3(kThreads), 0, s, p,
                          k_tiles);
   }();
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int q_tiles = (a.N + C::BM - 1) / C::BM;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, T>), dim3(static_cast<unsigned>(a.B) * a.Hq * q_tiles),
-                     dim3(kThreads), 0, s, p, q_tiles);
   return hipGetLastError();
 }
 

@@ -211,7 +211,7 @@ int attn_check_decode_args(const void* q, const void* k, const void* v,
  *          on entry do not matter, on return unspecified; must not overlap
  *          any other buffer; two calls in flight must not share it.
  *
- * Three kernels are queued on `stream`; the call never synchronises.  The
+ * Two kernels are queued on `stream`; the call never synchronises.  The
  * outputs must not overlap the inputs, each other or the workspace.  Every
  * pointer is 16-byte aligned (lse 4-byte).  Limits as for attn_fwd, and
  * B * Hq * round_up(N, 128) < 2^31.  Returns an attn_status value; on any
