@@ -3,9 +3,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 
-Without --warmup the warm-up runs for 0.3 s of steps (the GPU clock ramps up
-over the first ~40 ms of load), without --steps about 0.25 s of steps are
-timed; the JSON line reports the counts used.
+Every run first runs untimed steps for 0.3 s (the GPU clock ramps up over
+the first ~40 ms of load; the line reports this as "clock_warmup"), then the
+--warmup steps (default 10), then times --steps steps (default: about 0.25 s
+of them); the JSON line reports the counts used, the kernel time per step
+(mean, median, min from HIP events around every step) and the mean graphics
+clock over the timed steps.
 
 A step is one call of the whole hot path (one fused forward kernel) over one
 batch of synthetic fp16 inputs already resident in device memory.  The default
@@ -58,57 +61,150 @@ BACKWARD_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention
 BACKWARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_traffic.json")
 
 
-# Without --warmup, warm-up steps run until WARMUP_S seconds have passed: the
-# MI355X clock ramps up over the first ~40 ms of load after idle (a forward
-# step of the LLaMA-7B layer shape takes 266 us in its first 20 steps, 145 us
-# after 20 ms and 138 us from ~60 ms on), so a few steps would time the ramp,
-# not the kernel.  Without --steps, the timed region is about TIMED_S seconds
-# of steps (at least 5).
-WARMUP_S = 0.3
+# Before the requested warm-up steps, steps run for CLOCK_WARMUP_S seconds
+# (always, with the count reported as its own field): the MI355X clock ramps
+# up over the first ~40 ms of load after idle (a forward step of the LLaMA-7B
+# layer shape takes 266 us in its first 20 steps, 145 us after 20 ms and
+# 138 us from ~60 ms on), so a few warm-up steps on an idle GPU would time
+# the ramp, not the kernel.  Without --steps, the timed region is about
+# TIMED_S seconds of steps (at least 5).
+CLOCK_WARMUP_S = 0.3
 TIMED_S = 0.25
+DEFAULT_WARMUP = 10
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (MHz) from the driver's metrics table
+    (amdsmi) in a background thread while the timed steps run; reports None
+    where the metrics cannot be read."""
+
+    def __init__(self, period_s: float = 0.002):
+        self.period_s = period_s
+        self.samples = []
+        self.error = None
+        self._stop = None
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._handle = handles[0] if handles else None
+            if self._handle is not None and self._read() is None:
+                self._handle = None
+                self.error = "no graphics clock in the metrics table"
+        except Exception as e:  # no driver access: the figure is reported as null
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        vals = []
+        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+            x = m.get(key)
+            xs = x if isinstance(x, (list, tuple)) else [x]
+            vals = [float(v) for v in xs if isinstance(v, (int, float)) and 0 < v < 10000]
+            if vals:
+                return sum(vals) / len(vals)
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        import threading
+        if self._handle is None:
+            return
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if not self.samples:
+            return {"mean_mhz": None, "samples": 0, "source": "amdsmi gpu_metrics", "error": self.error}
+        xs = sorted(self.samples)
+        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": xs[0], "max_mhz": xs[-1],
+                "samples": len(xs), "source": "amdsmi gpu_metrics (current graphics clock, every ~2 ms)"}
 
 
 def run_timed(step, args, dev):
-    """Runs the warm-up and the timed steps of `step(i)`; sets args.warmup
-    and args.steps to the counts used and returns (wall ms per step, mean
-    step ms from one pair of HIP events on the launch stream)."""
+    """Runs the clock warm-up, the requested warm-up steps and the timed
+    steps of `step(i)`; sets args.warmup and args.steps to the counts used.
+    Returns (wall ms per step, kernel-time stats, clock-warm-up record, SCLK
+    record).  The kernel times come from HIP events recorded on the launch
+    stream before every timed step and after the last one: the mean is the
+    region's time over the steps, median and min are over the per-step
+    intervals."""
     import torch
 
-    if args.warmup is not None:
-        for i in range(args.warmup):
-            step(i)
+    n, t_start = 0, time.perf_counter()
+    while True:
+        t_batch = time.perf_counter()
+        for _ in range(10):
+            step(n)
+            n += 1
         torch.cuda.synchronize()
-        per_step = None
-    else:
-        n, t_start = 0, time.perf_counter()
-        while True:
-            t_batch = time.perf_counter()
-            for _ in range(10):
-                step(n)
-                n += 1
-            torch.cuda.synchronize()
-            now = time.perf_counter()
-            per_step = (now - t_batch) / 10
-            if now - t_start >= WARMUP_S:
-                break
-        args.warmup = n
-    if args.steps is None:
-        args.steps = 50 if per_step is None else max(5, min(5000, int(round(TIMED_S / per_step))))
-    # One pair of HIP events on the launch stream brackets the timed region
-    # (per-step events would add their own timestamp writes to every step);
-    # the kernel's average duration is the region's time over the steps.
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+        now = time.perf_counter()
+        per_step = (now - t_batch) / 10
+        if now - t_start >= CLOCK_WARMUP_S:
+            break
+    ramp = {"seconds": CLOCK_WARMUP_S, "steps": n,
+            "why": "untimed steps before the warm-up count, so that the timed steps do not see the clock ramp "
+                   "of an idle GPU"}
+    if args.warmup is None:
+        args.warmup = DEFAULT_WARMUP
+    for i in range(args.warmup):
+        step(n + i)
     torch.cuda.synchronize()
+    if args.steps is None:
+        args.steps = max(5, min(5000, int(round(TIMED_S / per_step))))
+    stream = torch.cuda.current_stream(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    clock = ClockSampler()
+    torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
-    ev0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
-    ev1.record(stream)
+        evs[i].record(stream)
+        step(n + args.warmup + i)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / args.steps, ev0.elapsed_time(ev1) / args.steps
+    sclk = clock.stop()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    stats = {"mean": evs[0].elapsed_time(evs[-1]) / args.steps, "median": per[len(per) // 2], "min": per[0],
+             "max": per[-1]}
+    return (t1 - t0) * 1e3 / args.steps, stats, ramp, sclk
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def kernel_ms_record(stats, steps: int, kernels: str) -> dict:
+    return {"mean": round(stats["mean"], 5), "median": round(stats["median"], 5), "min": round(stats["min"], 5),
+            "max": round(stats["max"], 5),
+            "timing": f"HIP events on the launch stream before each of the {steps} timed steps and after the "
+                      f"last ({kernels}); mean = region time / steps, median/min/max over the per-step intervals"}
 
 
 def kernel_source_hash(sources=FORWARD_SOURCES) -> str:
@@ -164,41 +260,56 @@ def cpu_threads() -> int:
 
 
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, budget_s: float, bf16: bool = False):
-    """Time the fp64 oracle on whole heads of the workload until ~budget_s of
-    CPU work is done; also check the GPU output of those heads against it."""
+    """Time the fp64 oracle on whole heads of the workload (on the workload's
+    seeded sample of query rows per head where it names one, the long-context
+    workload's 256) until ~budget_s of CPU work is done; also check the GPU
+    output of those rows against it."""
     import numpy as np
 
+    from exact_attention_121_amd.inputs import sample_rows
     from oracle.attention import attention_ref
 
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    done, elapsed = 0, 0.0
+    rows = sample_rows(w) if w.sample_rows else None
+    done, elapsed, pairs = 0, 0.0, 0
     max_err = mean_acc = lse_err = 0.0
     G = w.Hq // w.Hkv
     for b, h in heads:
         g = h // G
         qs, ks, vs = q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1]
+        r = None if rows is None else rows[b, h]
         t0 = time.perf_counter()
-        O_ref, L_ref = attention_ref(qs, ks, vs, w.scale, causal=w.causal)
+        O_ref, L_ref = attention_ref(qs, ks, vs, w.scale, causal=w.causal, rows=r)
         elapsed += time.perf_counter() - t0
-        err = np.abs(o_gpu[b, h].astype(np.float64) - O_ref[0, 0])
+        og = o_gpu[b, h] if r is None else o_gpu[b, h][r]
+        lg = lse_gpu[b, h] if r is None else lse_gpu[b, h][r]
+        err = np.abs(og.astype(np.float64) - O_ref[0, 0])
         max_err = max(max_err, float(err.max()))
         mean_acc += float(err.mean())
-        lse_err = max(lse_err, float(np.abs(lse_gpu[b, h] - L_ref[0, 0]).max()))
+        lse_err = max(lse_err, float(np.abs(lg - L_ref[0, 0]).max()))
+        if r is None:
+            pairs += w.pairs // len(heads)
+        else:
+            pairs += int(np.sum(r + 1)) if w.causal else len(r) * w.N
         done += 1
         if elapsed >= budget_s:
             break
-    per_head = w.flops / len(heads)
-    value = done * per_head / elapsed / 1e12
+    value = pairs * 4 * w.d / elapsed / 1e12
+    what = (f"all {w.N} query rows each" if rows is None
+            else f"the seeded sample of {rows.shape[2]} query rows each (rows 0 and N-1 and {rows.shape[2] - 2} "
+                 "drawn without replacement)")
     base = {
         "value": value,
         "unit": "TFLOP/s",
         "cores": cpu_threads(),
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
-        "sample": f"{done} of {len(heads)} (batch, head) pairs, all {w.N} query rows each, "
-                  f"{elapsed:.1f} s of fp64 numpy two-pass attention",
+        "sample": f"{done} of {len(heads)} (batch, head) pairs, {what}, {elapsed:.1f} s of fp64 numpy two-pass "
+                  "attention; TFLOP/s counts 4 d FLOPs per visible (query, key) pair of those rows",
     }
     bar = (4e-2, 4e-3, 4e-3) if bf16 else (1e-2, 1e-3, 1e-3)
-    parity = {"heads_checked": done, "max_abs_err_O": max_err, "mean_abs_err_O": mean_acc / done,
+    parity = {"heads_checked": done, "rows_per_head": "all" if rows is None else int(rows.shape[2]),
+              "max_abs_err_O": max_err, "mean_abs_err_O": mean_acc / done,
               "max_abs_err_LSE": lse_err, "bar": bar,
               "ok": bool(max_err <= bar[0] and mean_acc / done <= bar[1] and lse_err <= bar[2])}
     return base, parity
@@ -245,6 +356,7 @@ def cpu_baseline_decode(w, q, k, v, o_gpu, lse_gpu, budget_s: float):
         "value": value,
         "unit": "GB/s",
         "cores": cpu_threads(),
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
         "sample": f"{done} of {w.B} batch entries (all {w.Hq} query heads, all {w.Nk} keys each), "
                   f"{elapsed:.1f} s of fp64 numpy two-pass attention; GB/s counts the same "
@@ -281,7 +393,8 @@ def run_decode(args) -> int:
         kc, vc = kvs[i % copies]
         ea.attn_decode(q, kc, vc, scale=w.scale, causal=w.causal, out=o, lse=lse, workspace=ws)
 
-    ms_per_step, avg_step_ms = run_timed(step, args, dev)
+    ms_per_step, stats, ramp, sclk = run_timed(step, args, dev)
+    avg_step_ms = stats["mean"]
     value = w.hbm_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = w.hbm_bytes / (avg_step_ms * 1e-3) / 1e9
     result = {
@@ -305,8 +418,9 @@ def run_decode(args) -> int:
                      "traffic": measured_traffic(w.name, DECODE_TRAFFIC_FILE, DECODE_SOURCES, "hbm_bytes_per_step"),
                      "bytes_per_step": w.hbm_bytes,
                      "scope": "whole step: per-chunk kernel plus merge kernel"},
-        "kernel_ms": {"mean": round(avg_step_ms, 5), "timing": "HIP events on the launch stream around "
-                      f"all {args.steps} timed steps (one or two kernels per step)"},
+        "kernel_ms": kernel_ms_record(stats, args.steps, "one or two kernels per step"),
+        "clock_warmup": ramp,
+        "sclk": sclk,
         "kernel_code_sha256_16": kernel_source_hash(DECODE_SOURCES),
     }
     if args.calibrate_copy_mib > 0:
@@ -359,6 +473,7 @@ def cpu_baseline_backward(w, q, k, v, do, grads, budget_s: float, bf16: bool = F
         "value": done * per_head / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": cpu_threads(),
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} (batch, head) pairs, all {w.N} rows each, {elapsed:.1f} s of fp64 "
                   "numpy chain-rule backward",
@@ -395,7 +510,8 @@ def run_backward(args) -> int:
     def step(_i):
         ea.attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    ms_per_step, avg_step_ms = run_timed(step, args, dev)
+    ms_per_step, stats, ramp, sclk = run_timed(step, args, dev)
+    avg_step_ms = stats["mean"]
     flops = 10 * w.d * w.pairs
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_step_ms * 1e-3) / 1e12
@@ -422,8 +538,9 @@ def run_backward(args) -> int:
                                                                    "hbm_bytes_per_step"),
                      "flops_per_step": flops,
                      "scope": "whole step: dQ (with the row terms) and dK/dV kernels; 10 d FLOPs per visible pair"},
-        "kernel_ms": {"mean": round(avg_step_ms, 5), "timing": "HIP events on the launch stream around "
-                      f"all {args.steps} timed steps (two kernels per step)"},
+        "kernel_ms": kernel_ms_record(stats, args.steps, "two kernels per step"),
+        "clock_warmup": ramp,
+        "sclk": sclk,
         "kernel_code_sha256_16": kernel_source_hash(BACKWARD_SOURCES),
     }
     if args.calibrate_copy_mib > 0:
@@ -443,7 +560,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: about %.2f s of them)" % TIMED_S)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warm-up steps (default: as many as run in %.1f s)" % WARMUP_S)
+                    help="untimed warm-up steps after the %.1f s clock warm-up (default %d)"
+                         % (CLOCK_WARMUP_S, DEFAULT_WARMUP))
     ap.add_argument("--workload", type=int, default=2, help="named workload id (1-5)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
@@ -497,7 +615,8 @@ def main() -> int:
     def step(_i):
         ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
 
-    ms_per_step, avg_kernel_ms = run_timed(step, args, dev)
+    ms_per_step, stats, ramp, sclk = run_timed(step, args, dev)
+    avg_kernel_ms = stats["mean"]
 
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (avg_kernel_ms * 1e-3) / 1e12
@@ -523,8 +642,9 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic if args.dtype == "f16" else None},
-        "kernel_ms": {"mean": round(avg_kernel_ms, 5), "timing": "HIP events on the launch stream around "
-                      f"all {args.steps} timed steps"},
+        "kernel_ms": kernel_ms_record(stats, args.steps, "one kernel per step"),
+        "clock_warmup": ramp,
+        "sclk": sclk,
         "kernel_code_sha256_16": kernel_source_hash(),
     }
     if args.calibrate_copy_mib > 0:

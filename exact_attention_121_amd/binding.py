@@ -45,11 +45,15 @@ class AttnArgumentError(AttnError, ValueError):
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
-    """Load libattn_fwd.so once and declare its signatures."""
+    """Load libattn_fwd.so once and declare its signatures.  With a path, that
+    build of the library (e.g. a variant from build.variant_path) is loaded
+    and returned instead, without replacing the default one.  The environment
+    variable ATTN_LIBRARY names another default build (the CPU tests use it to
+    run against a sanitizer build of the host code)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("ATTN_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(
             f"{p} is missing: build it with `python -m exact_attention_121_amd.build` "
@@ -122,8 +126,23 @@ def _raise_for(status: int):
     raise AttnError(status, msg)
 
 
+def _keep_for_stream(s, *tensors):
+    """Marks tensors this module allocated on the current stream as used by
+    stream ``s`` when the kernels run there: torch's caching allocator then
+    waits for the work queued on ``s`` before it hands their memory to another
+    allocation (the decode partials and the backward's per-row terms are
+    written by one kernel and read by a later one, after the call returns)."""
+    import torch
+
+    if s == torch.cuda.current_stream(s.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def attn_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, out=None,
-             lse=None, return_lse: bool = True, stream=None):
+             lse=None, return_lse: bool = True, stream=None, library=None):
     """Fused attention forward on torch fp16 or bf16 tensors resident on one AMD GPU.
 
     q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous torch.float16 (or all
@@ -131,6 +150,8 @@ def attn_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, out=N
     [B, Hq, N, d] fp16 and lse [B, Hq, N] fp32 (None if return_lse is False
     and no lse buffer is given).  The kernel is queued on ``stream`` (a
     torch.cuda.Stream) or on torch's current stream of q's device.
+    ``library``: a library handle from load_library(path) to call instead of
+    the default build.
     """
     import torch
 
@@ -156,20 +177,24 @@ def attn_fwd(q, k, v, *, scale: float | None = None, causal: bool = False, out=N
     if scale is None:
         scale = 1.0 / math.sqrt(d)
 
+    made = []
     if out is None:
         out = torch.empty_like(q)
+        made.append(out)
     elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
           or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor of q's dtype, shaped like q on q's device")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        made.append(lse)
     elif lse is not None and (lse.shape != (B, Hq, N) or lse.dtype != torch.float32
                               or lse.device != q.device or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, N] on q's device")
 
-    lib = load_library()
+    lib = library if library is not None else load_library()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        _keep_for_stream(s, *made)
         fn = lib.attn_fwd_bf16 if q.dtype == torch.bfloat16 else lib.attn_fwd
         status = fn(
             q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
@@ -193,7 +218,7 @@ def attn_check_decode_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, worksp
 
 
 def attn_decode(q, k, v, *, scale: float | None = None, causal: bool = True, out=None, lse=None,
-                return_lse: bool = True, workspace=None, stream=None):
+                return_lse: bool = True, workspace=None, stream=None, library=None):
     """Decode step on torch fp16 (or bf16) tensors: q [B, Hq, Nq, d] are the last Nq
     positions of a sequence whose keys/values k, v [B, Hkv, Nk, d] are
     cached (Nq <= Nk).  With causal, query i sees keys 0 .. Nk - Nq + i.
@@ -224,26 +249,31 @@ def attn_decode(q, k, v, *, scale: float | None = None, causal: bool = True, out
     Hkv, Nk = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    made = []
     if out is None:
         out = torch.empty_like(q)
+        made.append(out)
     elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
           or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor of q's dtype, shaped like q on q's device")
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+        made.append(lse)
     elif lse is not None and (lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32
                               or lse.device != q.device or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq] on q's device")
     need = attn_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        made.append(workspace)
     elif workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
 
-    lib = load_library()
+    lib = library if library is not None else load_library()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        _keep_for_stream(s, *made)
         fn = lib.attn_decode_bf16 if q.dtype == torch.bfloat16 else lib.attn_decode
         status = fn(
             q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
@@ -269,7 +299,7 @@ def attn_check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, sca
 
 
 def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool = False, dq=None, dk=None,
-             dv=None, workspace=None, stream=None):
+             dv=None, workspace=None, stream=None, library=None):
     """Attention backward on torch tensors resident on one AMD GPU.
 
     q, o, dout: [B, Hq, N, d] and k, v: [B, Hkv, N, d], all fp16 or all bf16, with o and
@@ -306,10 +336,11 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool 
     Hkv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    outs = []
+    outs, made = [], []
     for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t is None:
             t = torch.empty_like(like)
+            made.append(t)
         elif (t.shape != like.shape or t.dtype != q.dtype or t.device != q.device
               or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous tensor of q's dtype shaped like its input")
@@ -318,13 +349,15 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool 
     need = attn_bwd_workspace_size(B, Hq, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        made.append(workspace)
     elif workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
 
-    lib = load_library()
+    lib = library if library is not None else load_library()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        _keep_for_stream(s, *made)
         fn = lib.attn_bwd_bf16 if q.dtype == torch.bfloat16 else lib.attn_bwd
         status = fn(
             q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
@@ -333,3 +366,4 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool 
             workspace.data_ptr() or None, ws_bytes, s.cuda_stream or None)
     _raise_for(status)
     return dq, dk, dv
+

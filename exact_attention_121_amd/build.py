@@ -6,10 +6,24 @@ The library is compiled with hipcc (cross-compilation works without a GPU)
 into ``exact_attention_121_amd/lib/libattn_fwd.so``; object files go to
 ``exact_attention_121_amd/_build/``.  Every HIP source is compiled with the
 packed-fp32 instructions disabled (``-target-feature -packed-fp32-ops``).
+
+Besides the default library, ``build()`` compiles the variants in VARIANTS
+into ``lib/variants/libattn_fwd_<name>.so``: the same sources with other
+compile-time settings, loaded only by the tests that hold them to the default
+build or to the oracle:
+
+* ``paranoid``: -DATTN_PARANOID_SYNC, every copy and LDS access completed and
+  a workgroup barrier at each phase boundary of the pipelined loops (the
+  race check: its outputs must equal the default build's bit for bit);
+* the tile variants of the offline sweep that the GPU tests run against the
+  oracle (other key-tile sizes or workgroups per CU than the defaults).
+
+The sources compile in parallel (one hipcc per source and variant).
 """
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -20,11 +34,24 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattn_fwd.so")
+VARIANT_DIR = os.path.join(LIB_DIR, "variants")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["attn_fwd_kernel.hip", "attn_decode_kernel.hip", "attn_bwd_kernel.hip"]
 CXX_SOURCES = ["attn_api.cpp"]
 DEPS = ["attn_launch.h", "attn_tile.h", os.path.join("..", "..", "include", "attn_fwd.h")]
+
+# name -> (extra hipcc flags, the HIP sources they change; the others are
+# shared with the default build)
+VARIANTS = {
+    "paranoid": (["-DATTN_PARANOID_SYNC"], HIP_SOURCES),
+    # 32-key tiles for head_dim 64 and 128 (the sweep's runner-up there)
+    "bn32": (["-DATTN_BN64=32", "-DATTN_BN128=32"], ["attn_fwd_kernel.hip"]),
+}
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(VARIANT_DIR, f"libattn_fwd_{name}.so")
 
 
 def _hipcc() -> str:
@@ -41,33 +68,61 @@ def hip_flags(extra=()) -> list[str]:
 
 
 def _run(cmd, verbose):
-    if verbose:
-        print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    if verbose and (res.stdout or res.stderr):
-        print(res.stdout + res.stderr, flush=True)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+        if res.stdout or res.stderr:
+            print(res.stdout + res.stderr, flush=True)
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source and link libattn_fwd.so; returns its path."""
+def _jobs() -> int:
+    for var in ("MAX_JOBS", "CMAKE_BUILD_PARALLEL_LEVEL"):
+        v = os.environ.get(var, "")
+        if v.isdigit() and int(v) > 0:
+            return min(int(v), 16)
+    return max(1, min(8, len(os.sched_getaffinity(0))))
+
+
+def build(verbose: bool = False, extra_flags=(), variants=True) -> str:
+    """Compile every source and link libattn_fwd.so (and the variants unless
+    variants is False); returns the default library's path."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
-    objs = []
+    compiles = []  # (command, object)
+    default_objs = {}
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run([hipcc, *hip_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        compiles.append([hipcc, *hip_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj])
+        default_objs[src] = obj
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run([hipcc, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c",
-              os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
+        compiles.append([hipcc, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c",
+                         os.path.join(CSRC, src), "-o", obj])
+        default_objs[src] = obj
+    links = [(LIB_PATH, [default_objs[s] for s in HIP_SOURCES + CXX_SOURCES])]
+    if variants:
+        os.makedirs(VARIANT_DIR, exist_ok=True)
+        for name, (flags, changed) in VARIANTS.items():
+            objs = []
+            for src in HIP_SOURCES + CXX_SOURCES:
+                if src in changed:
+                    obj = os.path.join(BUILD_DIR, f"{src}.{name}.o")
+                    compiles.append([hipcc, *hip_flags([*extra_flags, *flags]), "-c", os.path.join(CSRC, src),
+                                     "-o", obj])
+                    objs.append(obj)
+                else:
+                    objs.append(default_objs[src])
+            links.append((variant_path(name), objs))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=_jobs()) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd in compiles]:
+            f.result()
+    for path, objs in links:
+        tmp = path + ".tmp"
+        _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -225,37 +225,42 @@ extern "C" int attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t N, int64_t
   return ATTN_OK;
 }
 
-extern "C" int attn_check_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                                   const void* dout, const void* dq, const void* dk, const void* dv, int64_t B,
-                                   int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
-                                   const void* workspace, int64_t workspace_bytes) {
+namespace {
+
+// The validation of attn_bwd; with own_workspace false the workspace
+// arguments are not looked at.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              const void* dq, const void* dk, const void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+              float scale, const void* workspace, int64_t workspace_bytes, bool own_workspace) {
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   if (!head_dim_supported(d)) return ATTN_ERR_UNSUPPORTED;
   if (B == 0 || N == 0) return ATTN_OK;  // empty problem: nothing to touch
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
-      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
+      dq == nullptr || dk == nullptr || dv == nullptr || (own_workspace && workspace == nullptr))
     return ATTN_ERR_INVALID_ARG;
   if (misaligned_tensors(q, k, v, o, lse) || misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) ||
-      misaligned(dv, 16) || misaligned(workspace, 16))
+      misaligned(dv, 16) || (own_workspace && misaligned(workspace, 16)))
     return ATTN_ERR_INVALID_ARG;
   if (N > kLimitHead / d) return ATTN_ERR_INVALID_ARG;
   if (Hq >= kLimit31 || B >= kLimit31 / Hq) return ATTN_ERR_INVALID_ARG;
   const int64_t q_tiles = (N + kRowsPerBlock - 1) / kRowsPerBlock;
-  // Workgroups of the dQ and dK/dV kernels, and of the per-row preparation
-  // (d / 8 lanes per row), each below 2^24; padded rows fit in int.
+  // Workgroups of the dQ kernel (one per query tile) below 2^24; the dK/dV
+  // kernel has at most as many (one per 128 keys of a K/V head, twice that
+  // only on grids of fewer than 512).  The workspace rows (padded to whole
+  // query tiles) are indexed with 32-bit integers.
   if (B * Hq >= kLimitGroups / q_tiles) return ATTN_ERR_INVALID_ARG;
   const int64_t rows = B * Hq * attn::bwd_padded_rows(N);
-  if (rows >= kLimit31 || rows / (256 / (d / 8)) >= kLimitGroups) return ATTN_ERR_INVALID_ARG;
-  if (workspace_bytes < attn::bwd_workspace_bytes(B, Hq, N)) return ATTN_ERR_INVALID_ARG;
+  if (rows >= kLimit31) return ATTN_ERR_INVALID_ARG;
+  if (own_workspace && workspace_bytes < attn::bwd_workspace_bytes(B, Hq, N)) return ATTN_ERR_INVALID_ARG;
   const int64_t q_bytes = B * Hq * N * d * 2;
   const int64_t kv_bytes = B * Hkv * N * d * 2;
   const int64_t lse_bytes = B * Hq * N * 4;
-  const int64_t ws_bytes = attn::bwd_workspace_bytes(B, Hq, N);
+  const int64_t ws_bytes = own_workspace ? attn::bwd_workspace_bytes(B, Hq, N) : 0;
   const void* ins[6] = {q, k, v, o, lse, dout};
   const int64_t in_bytes[6] = {q_bytes, kv_bytes, kv_bytes, q_bytes, lse_bytes, q_bytes};
-  const void* outs[4] = {dq, dk, dv, workspace};
+  const void* outs[4] = {dq, dk, dv, own_workspace ? workspace : nullptr};
   const int64_t out_bytes[4] = {q_bytes, kv_bytes, kv_bytes, ws_bytes};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
@@ -266,13 +271,22 @@ extern "C" int attn_check_bwd_args(const void* q, const void* k, const void* v, 
   return ATTN_OK;
 }
 
+}  // namespace
+
+extern "C" int attn_check_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                   const void* dout, const void* dq, const void* dk, const void* dv, int64_t B,
+                                   int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
+                                   const void* workspace, int64_t workspace_bytes) {
+  return check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace, workspace_bytes, true);
+}
+
 namespace {
 
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
                int causal, void* workspace, int64_t workspace_bytes, int bf16, struct ihipStream_t* stream) {
-  const int st = attn_check_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace,
-                                     workspace_bytes);
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace, workspace_bytes,
+                           true);
   if (st != ATTN_OK) return st;
   if (B == 0 || N == 0) return ATTN_OK;
   attn::BwdArgs a;

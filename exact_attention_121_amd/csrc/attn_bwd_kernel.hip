@@ -306,6 +306,7 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
     // (wave-uniform, as the matrix instructions need).
     const bool active = kw0 < N && !(CAUSAL && q0 + C::BN - 1 < kw0);
     issue(u + 1, st ^ 1);
+    paranoid_sync();
     if (active) {
       const float* lrow = rowterms + (2 * st) * 64;   // LSE (log2) of the tile's queries
       const float* drow = rowterms + (2 * st + 1) * 64;   // Delta of the tile's queries
@@ -376,6 +377,7 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
         }
       }
     }
+    paranoid_sync();
     wait_vm_all();
     __syncthreads();
     };
@@ -488,6 +490,7 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
     const uint32_t nb = tile_base<D>(j + 1, nt);
     load_tile<D>(krs, k_stage<D>(smem, st ^ 1), nb, lo, tid);
     load_tile<D>(vrs, v_stage<D>(smem, st ^ 1), nb, lo, tid);
+    paranoid_sync();
     if (j < nt_w) {
       STile<D> s, dp;
       qk_tile<D, T>(k_stage<D>(smem, st), qf, off, s);    // S^T = K Q^T
@@ -507,6 +510,7 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
       p_and_ds<D, T>(s, dp, dl, pf, dsf);
       pv_tile<D, T>(k_stage<D>(smem, st), dsf, off, dq_acc);   // dQ^T += K^T dS^T
     }
+    paranoid_sync();
     wait_vm_all();
     __syncthreads();
     };
@@ -596,5 +600,6 @@ int launch_backward(const BwdArgs& a, void* stream) {
   });
   return static_cast<int>(e);
 }
+
 
 }  // namespace attn

@@ -152,8 +152,10 @@ struct BwdArgs {
   int bf16;    // element type of q, k, v, o, dout and the gradients: 0 = fp16, 1 = bf16
 };
 
-// Queues the three backward kernels (prep, dK/dV, dQ) on `stream`.
+// Queues the two backward kernels on `stream`: dQ (which also writes the
+// per-row LSE and Delta terms to the workspace), then dK/dV.
 int launch_backward(const BwdArgs& a, void* stream);
+
 
 }  // namespace attn
 

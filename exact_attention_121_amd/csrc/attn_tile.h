@@ -289,6 +289,25 @@ __device__ __forceinline__ uint32_t tile_base(int j, int nt) {
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Race-check build (-DATTN_PARANOID_SYNC): at every phase boundary of the
+// pipelined loops all outstanding copies and LDS accesses complete and every
+// wave of the workgroup arrives.  The arithmetic and its order do not change,
+// so that build must give bit-for-bit the same outputs as the default one; a
+// difference would mean a stage was read before its copy landed or
+// overwritten while another wave still read it.  Called the same number of
+// times by every wave of a workgroup.
+#ifdef ATTN_PARANOID_SYNC
+constexpr bool kParanoidSync = true;
+#else
+constexpr bool kParanoidSync = false;
+#endif
+__device__ __forceinline__ void paranoid_sync() {
+  if constexpr (kParanoidSync) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+}
+
 __device__ __forceinline__ short4v tr_read(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
 }
@@ -667,6 +686,7 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
   if (UNIFORM || j < w.nt_w) {
     load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), v_base, lo, tid);
     load_tile<D>(krs, k_stage<D>(smem, PAR), k_base, lo, tid);
+    paranoid_sync();
     // S_{j+1} is computed even past this wave's last tile (reading a stale
     // but in-bounds stage) so that the matrix and vector work stay in one
     // block the scheduler can interleave; it is discarded then.
@@ -721,9 +741,12 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
     }
     __builtin_amdgcn_s_setprio(0);
     if (j + 1 < w.nt_w) raise_max<D>(m_tile, w.m_run, w.l_run, w.oacc);
+    paranoid_sync();
   } else {
     load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), v_base, lo, tid);
     load_tile<D>(krs, k_stage<D>(smem, PAR), k_base, lo, tid);
+    paranoid_sync();
+    paranoid_sync();
   }
   wait_vm_all();
   __syncthreads();

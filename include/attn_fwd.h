@@ -256,7 +256,7 @@ int attn_check_bwd_args(const void* q, const void* k, const void* v,
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 
-/* Static version string of the library, e.g. "attn_fwd 0.3.0 gfx950". */
+/* Static version string of the library, e.g. "attn_fwd 0.4.0 gfx950". */
 const char* attn_version(void);
 
 #ifdef __cplusplus

@@ -25,6 +25,7 @@ def _declared_functions():
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"^\s*#.*$", "", text, flags=re.M)  # preprocessor lines (macros, guards)
         for m in re.finditer(r"\b([A-Za-z_]\w*)\s*\(([^;{}]*)\)\s*;", text):
             names.add(m.group(1))
     return names
@@ -351,3 +352,15 @@ def test_bwd_binding_refuses_cpu_tensors():
     lse = torch.zeros(1, 1, 8)
     with pytest.raises(ValueError, match="AMD GPU"):
         ea.attn_bwd(x, x, x, x, lse, x)
+
+
+def test_bwd_accepts_large_head_counts_at_d256():
+    """B=1, Hq=64, N=2^21, d=256: 2^27 padded workspace rows and 2^20 dQ
+    workgroups are within the kernels' limits (a limit of an earlier
+    separate per-row pass, rows / 8 < 2^24, no longer applies); 2^31 rows are
+    not."""
+    T = 1 << 40  # pointers far enough apart for 2^36-byte tensors
+    ptrs = dict(q=T, k=2 * T, v=3 * T, o=4 * T, lse=5 * T, dout=6 * T, dq=7 * T, dk=8 * T, dv=9 * T,
+                workspace=10 * T)
+    assert bcheck(B=1, Hq=64, Hkv=64, N=1 << 21, d=256, **ptrs) == ea.ATTN_OK
+    assert bcheck(B=1, Hq=1024, Hkv=1024, N=1 << 21, d=256, **ptrs) == ea.ATTN_ERR_INVALID_ARG

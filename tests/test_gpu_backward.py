@@ -14,6 +14,7 @@ gradient; the mean is held to about the half-ulp.  Where the exact gradient
 is identically zero (a single key), |X_gpu| <= 1e-5.
 """
 
+import functools
 import sys
 
 import numpy as np
@@ -111,32 +112,49 @@ def test_backward_other_scales(scale):
         assert_grad_parity(got, ref, f"scale={scale} causal={causal}")
 
 
-@pytest.mark.parametrize("wid,heads", [(2, [(0, 0), (1, 31)]), (3, [(0, 0), (7, 15)])])
-def test_named_workload_backward(wid, heads):
-    """The LLaMA-7B layer shape (the backward bench line) and the spiky causal
-    prefill at full size; the oracle checks whole (batch, head) pairs."""
+@functools.lru_cache(maxsize=1)
+def _named_workload_backward(wid):
     w = WORKLOADS[wid]
-    _say(f"[bwd] workload {wid} {w.name}: {w.describe()}")
     q, k, v = make_inputs(w)
     do = make_dout(q.shape, seed=w.seed + 7)
-    got = gpu_backward(q, k, v, do, w.scale, w.causal)
-    for b, h in heads:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = attention_bwd_ref(q[sl], k[sl], v[sl], do[sl], w.scale, causal=w.causal)
-        assert_grad_parity([x[sl] for x in got], ref, f"{w.name} head ({b}, {h})")
+    return w, (q, k, v, do), gpu_backward(q, k, v, do, w.scale, w.causal)
 
 
-def test_gqa_workload_backward_one_group():
-    """The GQA workload (Hq 32, Hkv 8, N 8192, d 256) at full size; the oracle
-    checks key/value head 0 (its dK, dV sum over query heads 0-3) and the dQ
-    of those four heads."""
+@pytest.mark.parametrize("wid,batches", [(2, (0, 1)), (3, (0, 1, 2, 3)), (3, (4, 5, 6, 7))])
+def test_named_workload_backward(wid, batches):
+    """The LLaMA-7B layer shape (the backward bench line) and the spiky causal
+    prefill at full size; the oracle checks every (batch, head) pair of the
+    listed batch entries, so that the cases together cover every head."""
+    w, (q, k, v, do), got = _named_workload_backward(wid)
+    _say(f"[bwd] workload {wid} {w.name}: {w.describe()}, batch entries {batches}")
+    for b in batches:
+        for h in range(w.Hq):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            ref = attention_bwd_ref(q[sl], k[sl], v[sl], do[sl], w.scale, causal=w.causal)
+            assert_grad_parity([x[sl] for x in got], ref, f"{w.name} head ({b}, {h})")
+
+
+@functools.lru_cache(maxsize=1)
+def _gqa_workload_backward():
     w = WORKLOADS[4]
-    _say(f"[bwd] workload 4 {w.name}: {w.describe()}")
     q, k, v = make_inputs(w)
     do = make_dout(q.shape, seed=w.seed + 7)
-    got = gpu_backward(q, k, v, do, w.scale, w.causal)
-    ref = attention_bwd_ref(q[:, 0:4], k[:, 0:1], v[:, 0:1], do[:, 0:4], w.scale, causal=w.causal)
-    assert_grad_parity([got[0][:, 0:4], got[1][:, 0:1], got[2][:, 0:1]], ref, "gqa_causal group 0")
+    return w, (q, k, v, do), gpu_backward(q, k, v, do, w.scale, w.causal)
+
+
+@pytest.mark.parametrize("groups", [(0, 1), (2, 3), (4, 5), (6, 7)])
+def test_gqa_workload_backward(groups):
+    """The GQA workload (Hq 32, Hkv 8, N 8192, d 256) at full size; the oracle
+    checks every key/value head (its dK, dV sum over its four query heads)
+    and the dQ of every query head, two groups per test case."""
+    w, (q, k, v, do), got = _gqa_workload_backward()
+    G = w.Hq // w.Hkv
+    for g in groups:
+        _say(f"[bwd] workload 4 {w.name}: group {g} of {w.Hkv}")
+        qs = slice(g * G, (g + 1) * G)
+        ks = slice(g, g + 1)
+        ref = attention_bwd_ref(q[:, qs], k[:, ks], v[:, ks], do[:, qs], w.scale, causal=w.causal)
+        assert_grad_parity([got[0][:, qs], got[1][:, ks], got[2][:, ks]], ref, f"gqa_causal group {g}")
 
 
 @pytest.mark.parametrize("d", [32, 64, 96, 128, 160, 192, 224])

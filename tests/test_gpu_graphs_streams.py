@@ -134,3 +134,54 @@ def test_three_streams_at_once():
         assert all(torch.equal(a, b) for a, b in zip(c_f, r_f))
         assert all(torch.equal(a, b) for a, b in zip(c_d, r_d))
         assert all(torch.equal(a, b) for a, b in zip(c_b, r_b))
+
+
+def test_explicit_stream_without_workspace():
+    """stream= a side stream and no workspace: the binding allocates the
+    workspace on the current stream, the kernels use it on the side stream
+    after the call returns.  A long matrix product queued first keeps the side
+    stream busy while a buffer of the same size is allocated and filled on the
+    current stream; the results must still match the oracle (and an ordinary
+    call bit for bit)."""
+    import torch
+
+    from oracle.attention import attention_decode_ref
+    from oracle.backward import attention_bwd_ref
+
+    _say("[streams] backward and decode on an explicit side stream, workspace allocated by the binding")
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    qn, kn, vn = make_qkv(1, 4, 2, 300, 64, seed=95)
+    don = np.random.default_rng(96).standard_normal(qn.shape, dtype=np.float32).astype(np.float16)
+    q, k, v, do = to_dev(qn, kn, vn, don)
+    o, lse = ea.attn_fwd(q, k, v, causal=True)
+    dshape = (2, 8, 2, 1, 5000, 128)
+    dqn, dkn, dvn = make_decode_qkv(*dshape, seed=97)
+    dq_in, dk_in, dv_in = to_dev(dqn, dkn, dvn)
+    ref_b = ea.attn_bwd(q, k, v, o, lse, do, causal=True)
+    ref_d = ea.attn_decode(dq_in, dk_in, dv_in, causal=True)
+    big = torch.randn(4096, 4096, device=q.device)
+    torch.cuda.synchronize()
+    bws = ea.attn_bwd_workspace_size(1, 4, 300, 64)
+    dws = ea.attn_decode_workspace_size(*dshape)
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for _ in range(8):
+            big = big @ big * 1e-3  # keeps the side stream busy for a while
+    got_b = ea.attn_bwd(q, k, v, o, lse, do, causal=True, stream=side)
+    got_d = ea.attn_decode(dq_in, dk_in, dv_in, causal=True, stream=side)
+    # Same-size allocations on the current stream, filled with NaN bytes.
+    junk = [torch.full((n,), 0xFF, dtype=torch.uint8, device=q.device) for n in (bws, dws, bws, dws)]
+    torch.cuda.synchronize()
+    del junk
+    for name, g, r in zip(("dQ", "dK", "dV"), got_b, ref_b):
+        assert torch.equal(g, r), f"backward {name} on the side stream differs from the ordinary call"
+    assert torch.equal(got_d[0], ref_d[0]) and torch.equal(got_d[1], ref_d[1]), "decode differs"
+    refs = attention_bwd_ref(qn, kn, vn, don, float(np.float32(1 / 8)), causal=True)
+    for name, g, r in zip(("dQ", "dK", "dV"), got_b, refs):
+        err = np.abs(g.cpu().numpy().astype(np.float64) - r)
+        assert err.max() <= 1e-2 * np.abs(r).max() and err.mean() <= 2e-3 * np.abs(r).mean(), name
+    O_ref, L_ref = attention_decode_ref(dqn, dkn, dvn, float(np.float32(1 / np.sqrt(128))), causal=True)
+    err = np.abs(got_d[0].cpu().numpy().astype(np.float64) - O_ref)
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3
+    assert np.abs(got_d[1].cpu().numpy() - L_ref).max() <= 1e-3

@@ -3,9 +3,10 @@
 Bar: max |O_gpu - O_ref| <= 1e-2, mean |O_gpu - O_ref| <= 1e-3,
 |LSE_gpu - LSE_ref| <= 1e-3, no NaN/Inf.  The five named workloads run at
 their full sizes in the launch configuration the benchmark times; the oracle
-checks every row where it finishes in seconds and a seeded sample of 256
-query rows per head elsewhere, and properties that hold at any size (every
-output row inside the value range) are checked over all rows.
+checks every row of workloads 1-4 and a seeded sample of 256 query rows per
+head of the long-context workload (whose full check would take hours of
+fp64 work), and properties that hold at any size (every output row inside
+the value range) are checked over all rows.
 """
 
 import itertools
@@ -33,8 +34,19 @@ def test_named_workload(wid):
     o, lse = gpu_attention(q, k, v, w.scale, w.causal)
     assert np.isfinite(o.astype(np.float32)).all() and np.isfinite(lse).all()
     assert convex_hull_ok(o, v, w.Hq), "an output row left the value range"
-    if wid in (1, 2):
-        O_ref, L_ref = attention_ref(q, k, v, w.scale, causal=w.causal)
+    if wid != 5:
+        # Every row of every head against the oracle, one (batch, head) at a
+        # time (the causal prefill and GQA workloads take ~40 s of fp64 work
+        # on 8 host cores).
+        G = w.Hq // w.Hkv
+        O_ref = np.empty(o.shape, dtype=np.float64)
+        L_ref = np.empty(lse.shape, dtype=np.float64)
+        for b in range(w.B):
+            for h in range(w.Hq):
+                g = h // G
+                Oh, Lh = attention_ref(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], w.scale,
+                                       causal=w.causal)
+                O_ref[b, h], L_ref[b, h] = Oh[0, 0], Lh[0, 0]
         mx, mean = assert_parity(o, lse, O_ref, L_ref, what=w.name)
     else:
         rows = sample_rows(w, count=256)
