@@ -13,13 +13,16 @@ the in-tree build script and the seeded input generator.
 from .binding import (  # noqa: F401
     ATTN_ERR_DEVICE,
     ATTN_ERR_INVALID_ARG,
+    ATTN_ERR_SCRATCH,
     ATTN_ERR_UNSUPPORTED,
     ATTN_OK,
+    BWD_NOALLOC_SCRATCH_BYTES,
     EXPORTS,
     AttnArgumentError,
     AttnError,
     AttnUnsupportedError,
     attn_bwd,
+    attn_bwd_noalloc,
     attn_bwd_workspace_size,
     attn_check_args,
     attn_check_bwd_args,

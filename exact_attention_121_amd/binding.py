@@ -20,9 +20,11 @@ ATTN_OK = 0
 ATTN_ERR_INVALID_ARG = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_DEVICE = 3
+ATTN_ERR_SCRATCH = 4
+BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_check_args", "attn_decode", "attn_decode_bf16", "attn_decode_workspace_size",
-           "attn_check_decode_args", "attn_bwd", "attn_bwd_bf16", "attn_bwd_workspace_size", "attn_check_bwd_args",
+           "attn_check_decode_args", "attn_bwd", "attn_bwd_bf16", "attn_bwd_workspace_size", "attn_check_bwd_args", "attn_bwd_noalloc",
            "attn_status_string", "attn_version")
 
 _lib = None
@@ -93,6 +95,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_check_bwd_args.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                         ctypes.c_float, vp, i64]
     lib.attn_check_bwd_args.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                     ctypes.c_int, vp]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -367,3 +372,45 @@ def attn_bwd(q, k, v, o, lse, dout, *, scale: float | None = None, causal: bool 
     _raise_for(status)
     return dq, dk, dv
 
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, *, scale: float | None = None, causal: bool = False,
+                     stream=None):
+    """attn_bwd for fp16 tensors with the library's fixed scratch instead of a
+    workspace: neither this wrapper nor the library allocates anything, so the
+    outputs dq, dk, dv must be given.  For problems with B * Hq * round_up(N,
+    128) <= 2^21; larger ones raise (ATTN_ERR_SCRATCH).  Calls in flight at
+    once on one GPU share its scratch and must not overlap.
+    Returns (dq, dk, dv)."""
+    import torch
+
+    ts = (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv))
+    for name, t in ts:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.float16:
+            raise TypeError(f"{name} must be torch.float16, got {t.dtype}")
+        if t.device.type != "cuda" or t.device != q.device:
+            raise ValueError(f"{name} must be on q's AMD GPU (torch 'cuda' device), got {t.device}")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D [B, H, N, d] tensor")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape or dq.shape != q.shape:
+        raise ValueError("o, dout and dq must be shaped like q")
+    if dk.shape != k.shape or dv.shape != k.shape:
+        raise ValueError("dk and dv must be shaped like k")
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, Hq, N) or lse.dtype != torch.float32
+            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be the contiguous fp32 [B, Hq, N] tensor attn_fwd returned")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = lib.attn_bwd_noalloc(
+            q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None, o.data_ptr() or None,
+            lse.data_ptr() or None, dout.data_ptr() or None, dq.data_ptr() or None, dk.data_ptr() or None,
+            dv.data_ptr() or None, B, Hq, k.shape[1], N, d, float(scale), 1 if causal else 0, s.cuda_stream or None)
+    _raise_for(status)
+    return dq, dk, dv

@@ -227,8 +227,8 @@ extern "C" int attn_bwd_workspace_size(int64_t B, int64_t Hq, int64_t N, int64_t
 
 namespace {
 
-// The validation of attn_bwd; with own_workspace false the workspace
-// arguments are not looked at.
+// The validation of attn_bwd; with own_workspace false (attn_bwd_noalloc) the
+// workspace arguments are not looked at: the scratch is the library's own.
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
               const void* dq, const void* dk, const void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
               float scale, const void* workspace, int64_t workspace_bytes, bool own_workspace) {
@@ -282,13 +282,16 @@ extern "C" int attn_check_bwd_args(const void* q, const void* k, const void* v, 
 
 namespace {
 
+// own_workspace false: attn_bwd_noalloc (the library's fixed scratch).
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, float scale,
-               int causal, void* workspace, int64_t workspace_bytes, int bf16, struct ihipStream_t* stream) {
+               int causal, void* workspace, int64_t workspace_bytes, int bf16, struct ihipStream_t* stream,
+               bool own_workspace = true) {
   const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace, workspace_bytes,
-                           true);
+                           own_workspace);
   if (st != ATTN_OK) return st;
   if (B == 0 || N == 0) return ATTN_OK;
+  if (!own_workspace && attn::bwd_workspace_bytes(B, Hq, N) > attn::kBwdNoallocScratchBytes) return ATTN_ERR_SCRATCH;
   attn::BwdArgs a;
   a.q = q;
   a.k = k;
@@ -308,7 +311,8 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   a.scale = scale;
   a.causal = causal != 0;
   a.bf16 = bf16;
-  return attn::launch_backward(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+  const int e = own_workspace ? attn::launch_backward(a, stream) : attn::launch_backward_noalloc(a, stream);
+  return e == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
 }  // namespace
@@ -329,6 +333,15 @@ extern "C" int attn_bwd_bf16(const void* q, const void* k, const void* v, const 
                     1, stream);
 }
 
+static_assert(attn::kBwdNoallocScratchBytes == ATTN_BWD_NOALLOC_SCRATCH_BYTES, "scratch size mismatch");
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                                int64_t N, int64_t d, float scale, int causal, struct ihipStream_t* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, nullptr, 0, 0, stream,
+                    false);
+}
+
 extern "C" const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK:
@@ -339,6 +352,8 @@ extern "C" const char* attn_status_string(int status) {
       return "unsupported head_dim (must be a multiple of 32 from 32 to 256)";
     case ATTN_ERR_DEVICE:
       return "the HIP runtime refused the kernel launch";
+    case ATTN_ERR_SCRATCH:
+      return "problem too large for the fixed scratch of attn_bwd_noalloc (B * Hq * round_up(N, 128) > 2^21)";
     default:
       return "unknown status";
   }

@@ -39,9 +39,16 @@
 //   [CANN-FA]  www.mooersco.com/news/1200175
 //   [FA-Dict]  hwcomputing.csdn.net/6a0dbd08662f9a54cb75eb74.html
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn_tile.h"
+
+// Fixed scratch of the allocation-free backward (attn_bwd_noalloc): the
+// per-row LSE and Delta terms, 2 * 4 bytes per padded query row, for at most
+// 2^21 rows.  Each GPU the library runs on holds its own copy until the
+// process ends.
+static __device__ __align__(256) char scratch[attn::kBwdNoallocScratchBytes];
 
 namespace attn {
 namespace {
@@ -601,5 +608,35 @@ int launch_backward(const BwdArgs& a, void* stream) {
   return static_cast<int>(e);
 }
 
+
+// attn_bwd_noalloc: the per-row terms go to this fixed array instead of a
+// caller workspace.  In host code `scratch` names a host-side stand-in, not
+// the device memory: its device address is looked up once per device (with
+// that device current) and only that address is passed to the kernels.
+int launch_backward_noalloc(const BwdArgs& a, void* stream) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {
+      e = hipGetSymbolAddress(&ptrs[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        ptrs[dev] = nullptr;
+        return static_cast<int>(e);
+      }
+      if (ptrs[dev] == nullptr) return static_cast<int>(hipErrorInvalidSymbol);
+    }
+    ptr = ptrs[dev];
+  }
+  BwdArgs b = a;
+  b.workspace = ptr;
+  return launch_backward(b, stream);
+}
 
 }  // namespace attn

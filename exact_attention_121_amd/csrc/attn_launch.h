@@ -156,6 +156,12 @@ struct BwdArgs {
 // per-row LSE and Delta terms to the workspace), then dK/dV.
 int launch_backward(const BwdArgs& a, void* stream);
 
+// The allocation-free backward: a.workspace is ignored and replaced by the
+// library's fixed scratch array on the current device (kBwdNoallocScratchBytes;
+// the caller has checked bwd_workspace_bytes against it).  Returns the HIP
+// status of the address lookup or of the launches.
+constexpr int64_t kBwdNoallocScratchBytes = int64_t{16} << 20;
+int launch_backward_noalloc(const BwdArgs& a, void* stream);
 
 }  // namespace attn
 

@@ -71,7 +71,9 @@ enum attn_status {
                                non-finite scale, overlapping output, size over
                                limits, workspace too small */
   ATTN_ERR_UNSUPPORTED = 2, /* head_dim not a multiple of 32 in [32, 256] */
-  ATTN_ERR_DEVICE = 3       /* the HIP runtime refused the launch */
+  ATTN_ERR_DEVICE = 3,      /* the HIP runtime refused the launch */
+  ATTN_ERR_SCRATCH = 4      /* attn_bwd_noalloc: the problem needs more than
+                               ATTN_BWD_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 /*
@@ -252,6 +254,34 @@ int attn_check_bwd_args(const void* q, const void* k, const void* v,
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                         int64_t d, float scale, const void* workspace,
                         int64_t workspace_bytes);
+
+/* Bytes of the fixed scratch of attn_bwd_noalloc (per GPU). */
+#define ATTN_BWD_NOALLOC_SCRATCH_BYTES ((int64_t)16 << 20)
+
+/*
+ * attn_bwd_noalloc - attn_bwd (fp16) for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight training
+ * loops, harnesses that forbid allocation.  The same kernels, with the
+ * per-row terms kept in a fixed scratch array inside the library (one per
+ * GPU, ATTN_BWD_NOALLOC_SCRATCH_BYTES = 16 MiB, held until the process
+ * ends) instead of a caller workspace; the call allocates nothing.
+ *
+ *   Arguments as for attn_bwd without workspace and workspace_bytes.
+ *   Limit: attn_bwd_workspace_size(B, Hq, N, d) <= 16 MiB, i.e.
+ *          B * Hq * round_up(N, 128) <= 2^21 rows; larger problems return
+ *          ATTN_ERR_SCRATCH and launch nothing.
+ *   Every call on one GPU uses that GPU's scratch: two calls in flight at
+ *   once on the same GPU (e.g. on two streams) race and give wrong
+ *   gradients; calls on one stream, or on different GPUs, do not.  The
+ *   scratch needs no clearing (every row term is written before it is
+ *   read).  The first call on a device (the current one) looks up the
+ *   scratch's device address; ATTN_ERR_DEVICE if that fails.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk,
+                     void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                     int64_t d, float scale, int causal,
+                     struct ihipStream_t* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -364,3 +364,19 @@ def test_bwd_accepts_large_head_counts_at_d256():
                 workspace=10 * T)
     assert bcheck(B=1, Hq=64, Hkv=64, N=1 << 21, d=256, **ptrs) == ea.ATTN_OK
     assert bcheck(B=1, Hq=1024, Hkv=1024, N=1 << 21, d=256, **ptrs) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_bwd_noalloc_validates_on_the_host():
+    """attn_bwd_noalloc checks its arguments and its scratch limit before it
+    touches a device: B * Hq * round_up(N, 128) <= 2^21 rows."""
+    lib = ea.load_library()
+    T = 1 << 36
+    ptrs = [T * i for i in range(1, 10)]  # q, k, v, o, lse, dout, dq, dk, dv
+    assert lib.attn_bwd_noalloc(*ptrs, 1, 64, 8, 32768 + 1, 32, 0.125, 0, None) == ea.ATTN_ERR_SCRATCH
+    assert lib.attn_bwd_noalloc(*ptrs, 2, 64, 8, 32768, 32, 0.125, 0, None) == ea.ATTN_ERR_SCRATCH
+    nulls = [None] * 9
+    assert lib.attn_bwd_noalloc(*nulls, 1, 4, 2, 16, 64, 0.125, 1, None) == ea.ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd_noalloc(*ptrs, 1, 4, 2, 16, 80, 0.125, 1, None) == ea.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_bwd_noalloc(*ptrs, 1, 4, 3, 16, 64, 0.125, 1, None) == ea.ATTN_ERR_INVALID_ARG
+    assert lib.attn_bwd_noalloc(*nulls, 0, 4, 2, 16, 64, 0.125, 1, None) == ea.ATTN_OK
+    assert ea.attn_status_string(ea.ATTN_ERR_SCRATCH).startswith("problem too large")
