@@ -15,8 +15,12 @@ build or to the oracle:
 * ``paranoid``: -DATTN_PARANOID_SYNC, every copy and LDS access completed and
   a workgroup barrier at each phase boundary of the pipelined loops (the
   race check: its outputs must equal the default build's bit for bit);
-* the tile variants of the offline sweep that the GPU tests run against the
-  oracle (other key-tile sizes or workgroups per CU than the defaults).
+* ``bn32``: the runner-up tiles of the offline sweep (32-key tiles at
+  head_dim 128; one query block per wave and 64-key tiles at head_dim 64);
+* ``pp``: the 8-wave ping-pong form of the head_dim 128 non-causal forward
+  (two wave groups a phase apart, operands staged in registers a phase
+  ahead), measured slower than the default on gfx950;
+the GPU tests hold the last two to the oracle.
 
 The sources compile in parallel (one hipcc per source and variant).
 """
@@ -45,8 +49,11 @@ DEPS = ["attn_launch.h", "attn_tile.h", os.path.join("..", "..", "include", "att
 # shared with the default build)
 VARIANTS = {
     "paranoid": (["-DATTN_PARANOID_SYNC"], HIP_SOURCES),
-    # 32-key tiles for head_dim 64 and 128 (the sweep's runner-up there)
-    "bn32": (["-DATTN_BN64=32", "-DATTN_BN128=32"], ["attn_fwd_kernel.hip"]),
+    # the runner-up tiles of the sweep: 32-key tiles at head_dim 128, and at
+    # head_dim 64 one 32-row query block per wave with 64-key tiles
+    "bn32": (["-DATTN_BN128=32", "-DATTN_QB64=1", "-DATTN_BN64=64", "-DATTN_WG64=0"], ["attn_fwd_kernel.hip"]),
+    # the 8-wave ping-pong kernel for the head_dim 128 non-causal forward
+    "pp": (["-DATTN_FWD_PP=1"], ["attn_fwd_kernel.hip"]),
 }
 
 

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads, WGS) void attn_decode_split_kernel(DecPar
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) w.oacc[0][dt] = f32x16{};
   w.m_run[0] = -INFINITY;
-  w.l_run[0] = 0.f;
+  w.clear_sums(0);
 
   wait_vm_all();
   __syncthreads();
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, WGS) void attn_decode_split_kernel(DecPar
   // Partial result of this chunk for the rows that exist: O_s = O^T / l_s
   // (0 when the row saw no key) and LSE_s = m + log2 l_s (-inf when it saw
   // none).
-  const float l_tot = xlane_sum(w.l_run[0]);
+  const float l_tot = w.total_sum(0);
   if (!valid) return;
   if (p.splits == 1) {
     // One chunk holds every key (key 0 among them, so l_tot > 0): finish the

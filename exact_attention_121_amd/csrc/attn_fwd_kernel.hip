@@ -65,6 +65,23 @@
 //     tiles run heaviest first, interleaved across a group of heads so that
 //     the light tiles of the XCD's last heads fill the tail.
 
+// Tile configuration of this kernel at head_dim 64 (the offline tile sweep
+// overrides it with -D): two 32-row query blocks per wave, so that every K/V
+// operand read from LDS feeds two matrix instructions, with 32-key tiles so
+// that the registers still fit two workgroups per CU (222 per lane).
+// Measured on gfx950 against one block and 64-key tiles: +5.5 % on the
+// LLaMA-7B layer shape at d = 64, +1.3 % at N = 8192, +0.6 % on the spiky
+// causal prefill.  The decode and backward kernels keep the shared defaults.
+#ifndef ATTN_QB64
+#define ATTN_QB64 2
+#endif
+#ifndef ATTN_BN64
+#define ATTN_BN64 32
+#endif
+#ifndef ATTN_WG64
+#define ATTN_WG64 2
+#endif
+
 #include "attn_tile.h"
 
 namespace attn {
@@ -161,7 +178,7 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) w.oacc[qb][dt] = f32x16{};
     w.m_run[qb] = -INFINITY;
-    w.l_run[qb] = 0.f;
+    w.clear_sums(qb);
   }
 
   wait_vm_all();
@@ -195,12 +212,263 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
   for (int qb = 0; qb < C::QB; ++qb) {
     const int row = w.qrow + 32 * qb;
     const int row0 = w.qw0 + 32 * qb;
-    const float l_tot = xlane_sum(w.l_run[qb]);
+    const float l_tot = w.total_sum(qb);
     store_rows<D, T>(region, w.oacc[qb], 1.0f / l_tot, p.o + qoff + (size_t)row0 * D, N - row0, lane);
     if (p.lse != nullptr && w.g == 0 && row < N)
       p.lse[((size_t)b * p.Hq + hq) * N + row] = (w.m_run[qb] + __builtin_log2f(l_tot)) * kLn2;
   }
 }
+
+// ---------------------------------------------------------------------------
+// Ping-pong form: 512 threads = 8 waves, 256 query rows per workgroup (32 per
+// wave), 32-key K/V tiles.  Waves w and w + 4 share a SIMD.  The two wave
+// groups (waves 0-3 and 4-7) run the same program one phase apart, and every
+// phase ends at a workgroup barrier, so that on each SIMD one wave feeds the
+// matrix cores while the other only moves operands.  Per key tile j a wave
+// runs two phases:
+//   matrix phase j: S_{j+1} = K_{j+1} Q^T interleaved with O += P_{j-1} V_{j-1}
+//       (the dependent chain of the score product alternates with the four
+//       independent chains of the output product, so that no matrix
+//       instruction waits for its predecessor's result), while the vector
+//       ALUs take the row max of S_j (lazy raise of m) and P_j = exp2(c S_j - m)
+//       and add the row sums of P_{j-1};
+//   copy phase j: wait for this wave's share of the copies queued two tiles
+//       ago, queue K_{j+5} and V_{j+3}, and read the K_{j+2} and V_j operands
+//       from LDS into registers for the next matrix phase,
+// so every matrix instruction finds both operands in registers and the
+// softmax of one tile runs under the matrix work of its neighbours ([CANN-FA]
+// "Ascend C implementation" and "key design points": data movement
+// overlapped with the matrix unit).  Each group copies half of every tile
+// (rows 16 g .. 16 g + 15) with one 16-byte buffer-to-LDS load per thread;
+// K and V have four LDS stages each, separate objects so that the compiler
+// can tell a read of one stage from a copy in flight into another.
+template <int D>
+struct PPCfg {
+  static constexpr int BM = 256;                   // query rows per workgroup
+  static constexpr int BN = 32;                    // keys per K/V tile
+  static constexpr int DC = D / 16;                // 16-dim k-steps of Q.K
+  static constexpr int DT = D / 32;                // 32-dim row tiles of O^T
+  static constexpr int CPR = lds_row_chunks<D>();  // 16-byte chunks per LDS row
+  static constexpr int TILE = BN * CPR * 16;       // bytes of one K or V tile
+  static constexpr int KAHEAD = 5;                 // K_{j+5} is queued in copy phase j
+  static constexpr int VAHEAD = 3;                 // V_{j+3}
+  static_assert(CPR == 16 && D == 128, "the ping-pong form is built for head_dim 128");
+  static_assert(32 * CPR * 16 == TILE, "one wave's output rows fill one stage");
+};
+
+constexpr int kPPThreads = 512;
+constexpr int kSchedTrans = 0x400;
+
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Waits until at most two of this wave's buffer-to-LDS copies are in flight
+// (the two queued in the previous copy phase).
+__device__ __forceinline__ void wait_vm_two() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
+
+template <int D, typename T>
+__global__ __launch_bounds__(kPPThreads, 1) void attn_fwd_pp_kernel(Params p) {
+  using C = PPCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k2s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k3s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v2s[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v3s[C::TILE];
+  // i is a compile-time constant at every use.
+  auto kst = [&](int i) -> char* { return i == 0 ? k0s : i == 1 ? k1s : i == 2 ? k2s : k3s; };
+  auto vst = [&](int i) -> char* { return i == 0 ? v0s : i == 1 ? v1s : i == 2 ? v2s : v3s; };
+
+  const int u = xcd_work_index();
+  const int bh = u / p.q_tiles, qt = u - bh * p.q_tiles;
+  const int b = bh / p.Hq, hq = bh - b * p.Hq, kvh = hq / p.group;
+  const int N = p.N;
+  const size_t qoff = ((size_t)b * p.Hq + hq) * (size_t)N * D;
+  const size_t kvoff = ((size_t)b * p.Hkv + kvh) * (size_t)N * D;
+  const int head_bytes = static_cast<int>(static_cast<uint32_t>(N) * (D * 2));
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kvoff), (short)0, head_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kvoff), (short)0, head_bytes, kBufferWord3);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv >> 2;
+  const int g = lane >> 5;
+  const int qw0 = qt * C::BM + 32 * wv;
+  const int qrow = qw0 + (lane & 31);
+  const int nt = (N + C::BN - 1) / C::BN;
+  const float c = p.c;
+
+  // This thread's share of a tile copy: row 16 grp + t / 16 of the tile,
+  // LDS slot t % 16 of that row, which holds source chunk (t % 16) ^ f(row).
+  const int t = tid & 255;
+  const int crow = 16 * grp + (t >> 4);
+  const int cchunk = (swz<D>(crow, t & 15) >> 4) - crow * C::CPR;
+  const uint32_t csrc = static_cast<uint32_t>((crow * D + cchunk * 8) * 2);
+  const int cdst = (16 * grp * C::CPR + (t & ~63)) * 16;  // wave-uniform
+  auto copy = [&](__amdgpu_buffer_rsrc_t rs, char* stage, int tile) {
+    const uint32_t base = tile < nt ? static_cast<uint32_t>(tile) * (C::BN * D * 2) : kSkipTile;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(stage + cdst), 16, static_cast<int>(base + csrc), 0,
+                                             0, 0);
+  };
+
+  Offsets<D> off;
+  off.init(lane);
+  half8 kr[C::DC];      // K_{j+1} operands (A of S^T = K Q^T)
+  half8 vr[2][C::DT];   // V_{j-1}^T operands, per 16-key half
+  auto load_k = [&](const char* ks) {
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) kr[dc] = *reinterpret_cast<const half8*>(ks + off.kofs(dc));
+  };
+  auto load_v = [&](const char* vs) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int kb = 16 * h * C::CPR * 16;
+        const short4v lo = tr_read(vs + off.vofs(0, dt) + kb);
+        const short4v hi = tr_read(vs + off.vofs(1, dt) + kb);
+        vr[h][dt] = __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  };
+  // Keys past the end of the sequence get logit -inf.
+  auto mask_tail = [&](f32x16& s, int kv0) {
+    const int lim = N - 1 - kv0 - 4 * g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 8 * (r >> 2) + (r & 3) <= lim ? s[r] : -INFINITY;
+  };
+  auto row_max = [&](const f32x16& s) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    return xlane_max(mx) * c;
+  };
+
+  copy(krs, kst(0), 0);
+  copy(krs, kst(1), 1);
+  copy(krs, kst(2), 2);
+  copy(vrs, vst(0), 0);
+
+  QFrag<D> qf;
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) {
+    u32x4 x = qrow < N ? *reinterpret_cast<const u32x4*>(p.q + qoff + (size_t)qrow * D + 16 * dc + 8 * g)
+                       : u32x4{0u, 0u, 0u, 0u};
+    x = (x ^ p.q_sign) & p.q_keep;
+    qf[0][dc] = __builtin_bit_cast(half8, x);
+  }
+  f32x16 oacc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
+  float l_run = 0.f;
+
+  wait_vm_all();
+  __syncthreads();
+  f32x16 s_cur;  // S_j
+  load_k(kst(0));
+  s_cur = f32x16{};
+#pragma unroll
+  for (int dc = 0; dc < C::DC; ++dc) s_cur = mfma16<T>(kr[dc], qf[0][dc], s_cur);
+  float m_run = -INFINITY;  // raised to S_0's row max in matrix phase 0
+  load_k(kst(1));
+  load_v(vst(0));   // stands in for V_{-1}: multiplied by P_{-1} = 0
+  half8 pf[2] = {half8{}, half8{}};  // P_{j-1}
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  phase_barrier();  // every wave is done with K_0's stage
+  copy(krs, kst(3), 3);   // the copies of copy phases -2 and -1
+  copy(vrs, vst(1), 1);
+  copy(krs, kst(0), 4);
+  copy(vrs, vst(2), 2);
+  if (grp == 1) phase_barrier();  // the second group runs one phase behind
+
+  // Matrix phase and copy phase of tile j; ST = j % 4 (compile-time).
+  auto iteration = [&](auto stc, int j) {
+    constexpr int ST = decltype(stc)::value;
+    // Row max of S_j: raise m lazily (the rescale of O waits for this
+    // phase's P_{j-1} V_{j-1} products below).
+    float alpha = 1.0f;
+    bool raise = false;
+    if (j < nt) {
+      if ((j + 1) * C::BN > N) mask_tail(s_cur, j * C::BN);
+      const float m_tile = row_max(s_cur);
+      if (__any(m_tile > m_run + kLazy)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+        m_run = m_new;
+        raise = true;
+      }
+    }
+    l_run += row_sum16<T>(pf);  // P_{j-1}, before the rescale
+    f32x16 s_nxt = f32x16{};
+    half8 pn[2];
+#pragma unroll
+    for (int i = 0; i < C::DC; ++i) {
+      s_nxt = mfma16<T>(kr[i], qf[0][i], s_nxt);
+      oacc[i % C::DT] = mfma16<T>(vr[i / C::DT][i % C::DT], pf[i / C::DT], oacc[i % C::DT]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      pn[r >> 3][r & 7] = to_elem<T>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], c, -m_run)));
+#pragma unroll
+    for (int i = 0; i < C::DC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedTrans, 2, 0);
+    }
+    if (raise) {
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) oacc[dt] *= alpha;
+    }
+    pf[0] = pn[0];
+    pf[1] = pn[1];
+    s_cur = s_nxt;
+    phase_barrier();
+    // Copy phase: the copies queued two tiles ago have landed; queue
+    // K_{j+5} and V_{j+3}; K_{j+2} and V_j operands into registers.
+    wait_vm_two();
+    copy(krs, kst((ST + 1) & 3), j + C::KAHEAD);
+    copy(vrs, vst((ST + 3) & 3), j + C::VAHEAD);
+    load_k(kst((ST + 2) & 3));
+    load_v(vst(ST));
+    phase_barrier();
+  };
+  // Tiles 0 .. nt: the last matrix phase only adds P_{nt-1} V_{nt-1}.
+  int j = 0;
+  for (; j + 3 <= nt; j += 4) {
+    iteration(std::integral_constant<int, 0>{}, j);
+    iteration(std::integral_constant<int, 1>{}, j + 1);
+    iteration(std::integral_constant<int, 2>{}, j + 2);
+    iteration(std::integral_constant<int, 3>{}, j + 3);
+  }
+  if (j <= nt) iteration(std::integral_constant<int, 0>{}, j);
+  if (j + 1 <= nt) iteration(std::integral_constant<int, 1>{}, j + 1);
+  if (j + 2 <= nt) iteration(std::integral_constant<int, 2>{}, j + 2);
+  if (grp == 0) phase_barrier();
+  // Every copy (including the skipped ones past the end) and every LDS read
+  // is complete before the stages are reused for the output rows.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  phase_barrier();
+
+  char* region = wv == 0 ? k0s : wv == 1 ? k1s : wv == 2 ? k2s : wv == 3 ? k3s
+               : wv == 4 ? v0s : wv == 5 ? v1s : wv == 6 ? v2s : v3s;
+  const float l_tot = xlane_sum(l_run);
+  store_rows<D, T>(region, oacc, 1.0f / l_tot, p.o + qoff + (size_t)qw0 * D, N - qw0, lane);
+  if (p.lse != nullptr && g == 0 && qrow < N)
+    p.lse[((size_t)b * p.Hq + hq) * N + qrow] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+}
+
+// Compile-time switch of the head_dim 128, non-causal forward: 1 = the
+// ping-pong kernel above, 0 = the 4-wave pipelined kernel.
+#ifndef ATTN_FWD_PP
+#define ATTN_FWD_PP 0
+#endif
 
 template <int D, bool CAUSAL>
 hipError_t launch_t(const LaunchArgs& a, Params p, hipStream_t s) {
@@ -208,6 +476,15 @@ hipError_t launch_t(const LaunchArgs& a, Params p, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(a.B) * a.Hq * p.q_tiles;
   // Each head streams its K/V head (K and V, 16-bit elements) through L2.
   p.head_group = CAUSAL ? causal_head_group(grid, p.q_tiles, static_cast<int64_t>(a.N) * D * 4, a.Hq / a.Hkv) : 1;
+  if constexpr (D == 128 && !CAUSAL && ATTN_FWD_PP) {
+    p.q_tiles = (a.N + PPCfg<D>::BM - 1) / PPCfg<D>::BM;
+    const unsigned pgrid = static_cast<unsigned>(a.B) * a.Hq * p.q_tiles;
+    if (a.bf16)
+      hipLaunchKernelGGL((attn_fwd_pp_kernel<D, __bf16>), dim3(pgrid), dim3(kPPThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_pp_kernel<D, _Float16>), dim3(pgrid), dim3(kPPThreads), 0, s, p);
+    return hipGetLastError();
+  }
   if (a.bf16)
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, __bf16>), dim3(grid), dim3(kThreads), 0, s, p);
   else

@@ -159,7 +159,7 @@ template <int D, bool CAUSAL>
 constexpr int fwd_wg_per_cu() {
   constexpr int hook = D == 32 ? ATTN_WG32 : D == 64 ? ATTN_WG64 : D == 96 ? ATTN_WG96 : D == 128 ? ATTN_WG128
                      : D == 160 ? ATTN_WG160 : D == 192 ? ATTN_WG192 : D == 224 ? ATTN_WG224 : ATTN_WG256;
-  if (query_blocks<D>() != 1) return 1;
+  if (query_blocks<D>() != 1) return hook ? hook : 1;
   return hook ? hook : (D == 256 && CAUSAL ? 2 : static_cast<int>(default_wg_per_cu(D)));
 }
 // Operands read ahead: a longer run of them pays only with the register
@@ -194,7 +194,7 @@ struct Cfg {
   static constexpr int TILE_BYTES = BN * CPR * 16;   // one K (or V) tile in LDS
   static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
   // Workgroups per CU the register budget allows.
-  static constexpr int WG_PER_CU = QB == 1 ? wg_per_cu<D>() : 1;
+  static constexpr int WG_PER_CU = QB == 1 ? wg_per_cu<D>() : fwd_wg_per_cu<D, false>();
   // Matrix operands read from LDS ahead of their MFMA (K reads; twice as
   // many V transpose reads, two per MFMA).
   static constexpr int K_AHEAD = k_ahead<D>();
@@ -525,6 +525,31 @@ __device__ __forceinline__ void add_row_sums(const PTile<D>& pf, float (&l_run)[
   }
 }
 
+// Sum of the 16 probabilities of one lane's 32-key block (two half8 B
+// operands), in fp32 with v_dot2 (two partial sums for a shorter chain).
+template <typename T>
+__device__ __forceinline__ float row_sum16(const half8 (&pf)[2]) {
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const half8 x = pf[h];
+    if constexpr (std::is_same_v<T, __bf16>) {
+      const bf16x8 y = __builtin_bit_cast(bf16x8, x);
+      const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{y[0], y[1]}, one, l0, false);
+      l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{y[2], y[3]}, one, l1, false);
+      l0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{y[4], y[5]}, one, l0, false);
+      l1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{y[6], y[7]}, one, l1, false);
+    } else {
+      l0 = __builtin_amdgcn_fdot2(half2v{x[0], x[1]}, half2v{1.0f16, 1.0f16}, l0, false);
+      l1 = __builtin_amdgcn_fdot2(half2v{x[2], x[3]}, half2v{1.0f16, 1.0f16}, l1, false);
+      l0 = __builtin_amdgcn_fdot2(half2v{x[4], x[5]}, half2v{1.0f16, 1.0f16}, l0, false);
+      l1 = __builtin_amdgcn_fdot2(half2v{x[6], x[7]}, half2v{1.0f16, 1.0f16}, l1, false);
+    }
+  }
+  return l0 + l1;
+}
+
 // O^T += V^T P^T for one key tile.  The A operand pairs B slot j of lane
 // group g with key 8 (j/4) + 4 g + j%4 (+16 h, +32 t): two transpose reads of
 // four keys each from V in its natural [key][dim] layout, shared by every
@@ -608,6 +633,9 @@ struct WaveState {
   float m_run[Cfg<D>::QB], l_run[Cfg<D>::QB];
   float c;
   int N, qw0, qrow, g, nt_w;  // qrow: row of this lane in block 0; nt_w: key tiles this wave computes
+  __device__ __forceinline__ void clear_sums(int qb) { l_run[qb] = 0.f; }
+  // The row's sum l over every visible key (both lane halves).
+  __device__ __forceinline__ float total_sum(int qb) const { return xlane_sum(l_run[qb]); }
 };
 
 // Workgroup id -> position in the list of work, so that each of the 8 XCDs

@@ -7,8 +7,10 @@
   backward outputs must equal the default build's bit for bit: a stage read
   before its copy landed, or refilled while a wave still read it, would show
   as a difference.
-* Tile variant: the ``bn32`` build (32-key tiles at head_dim 64 and 128, the
-  offline sweep's runner-up there) is held to the fp64 oracle, like the
+* Tile variants: the ``bn32`` build (the offline sweep's runner-up tiles:
+  32-key tiles at head_dim 128, one query block per wave with 64-key tiles
+  at head_dim 64) and the ``pp`` build (the 8-wave ping-pong kernel for the
+  head_dim 128 non-causal forward) are held to the fp64 oracle, like the
   default build.
 """
 
@@ -110,3 +112,19 @@ def test_bn32_variant_against_the_oracle(shape):
     torch.cuda.synchronize()
     O_ref, L_ref = attention_ref(qn, kn, vn, scale, causal=causal)
     assert_parity(o.cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, what=f"bn32 {shape}")
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 2048, 128, False), (2, 3, 1, 777, 128, False), (1, 1, 1, 33, 128, False),
+                                   (1, 4, 2, 1000, 128, False)])
+def test_pp_variant_against_the_oracle(shape):
+    import torch
+
+    B, Hq, Hkv, N, d, causal = shape
+    _say(f"[variant pp] B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}")
+    qn, kn, vn = make_qkv(B, Hq, Hkv, N, d, seed=700 + N, spike_frac=0.01, spike_mult=8.0)
+    q, k, v = to_dev(qn, kn, vn)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    o, lse = ea.attn_fwd(q, k, v, scale=scale, causal=causal, library=_variant("pp"))
+    torch.cuda.synchronize()
+    O_ref, L_ref = attention_ref(qn, kn, vn, scale, causal=causal)
+    assert_parity(o.cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, what=f"pp {shape}")
