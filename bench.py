@@ -53,7 +53,8 @@ DECODE_METRIC = "attention decode HBM GB/s + % of MI355X HBM peak"
 BACKWARD_METRIC = "attention bwd TFLOP/s + % of MI355X fp16 MFMA peak"
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published figure
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published figure
-FORWARD_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_fwd_kernel.hip"]
+FORWARD_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_fwd_kernel.hip",
+                   "exact_attention_121_amd/csrc/attn_fwd_kernel_d64_one_block.hip"]
 DECODE_SOURCES = ["exact_attention_121_amd/csrc/attn_tile.h", "exact_attention_121_amd/csrc/attn_decode_kernel.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_traffic.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_traffic.json")

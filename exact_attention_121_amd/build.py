@@ -41,7 +41,8 @@ LIB_PATH = os.path.join(LIB_DIR, "libattn_fwd.so")
 VARIANT_DIR = os.path.join(LIB_DIR, "variants")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["attn_fwd_kernel.hip", "attn_decode_kernel.hip", "attn_bwd_kernel.hip"]
+HIP_SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_kernel_d64_one_block.hip", "attn_decode_kernel.hip",
+               "attn_bwd_kernel.hip"]
 CXX_SOURCES = ["attn_api.cpp"]
 DEPS = ["attn_launch.h", "attn_tile.h", os.path.join("..", "..", "include", "attn_fwd.h")]
 

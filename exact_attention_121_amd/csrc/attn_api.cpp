@@ -95,7 +95,9 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   a.scale = scale;
   a.causal = causal != 0;
   a.bf16 = bf16;
-  return attn::launch_forward(a, stream) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+  const bool one_block = d == 64 && attn::forward_d64_one_block(B, Hq, N, a.causal);
+  const int e = one_block ? attn::launch_forward_d64_one_block(a, stream) : attn::launch_forward(a, stream);
+  return e == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
 }  // namespace

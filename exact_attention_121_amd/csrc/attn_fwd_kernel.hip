@@ -472,6 +472,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void attn_fwd_pp_kernel(Params p) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_t(const LaunchArgs& a, Params p, hipStream_t s) {
+#ifdef ATTN_FP16_ONLY
+  if (a.bf16) return hipErrorInvalidValue;  // offline tile sweep builds: fp16 only
+#endif
   p.q_tiles = (a.N + Cfg<D>::BM - 1) / Cfg<D>::BM;
   const unsigned grid = static_cast<unsigned>(a.B) * a.Hq * p.q_tiles;
   // Each head streams its K/V head (K and V, 16-bit elements) through L2.
@@ -479,22 +482,31 @@ hipError_t launch_t(const LaunchArgs& a, Params p, hipStream_t s) {
   if constexpr (D == 128 && !CAUSAL && ATTN_FWD_PP) {
     p.q_tiles = (a.N + PPCfg<D>::BM - 1) / PPCfg<D>::BM;
     const unsigned pgrid = static_cast<unsigned>(a.B) * a.Hq * p.q_tiles;
+#ifndef ATTN_FP16_ONLY
     if (a.bf16)
       hipLaunchKernelGGL((attn_fwd_pp_kernel<D, __bf16>), dim3(pgrid), dim3(kPPThreads), 0, s, p);
     else
+#endif
       hipLaunchKernelGGL((attn_fwd_pp_kernel<D, _Float16>), dim3(pgrid), dim3(kPPThreads), 0, s, p);
     return hipGetLastError();
   }
+#ifndef ATTN_FP16_ONLY
   if (a.bf16)
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, __bf16>), dim3(grid), dim3(kThreads), 0, s, p);
   else
+#endif
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, _Float16>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int launch_forward(const LaunchArgs& a, void* stream) {
+// The entry point's name: launch_forward, or another name when this file is
+// compiled again with other tiles (attn_fwd_kernel_d64_one_block.hip).
+#ifndef ATTN_FWD_ENTRY
+#define ATTN_FWD_ENTRY launch_forward
+#endif
+int ATTN_FWD_ENTRY(const LaunchArgs& a, void* stream) {
   Params p;
   p.q = static_cast<const _Float16*>(a.q);
   p.k = static_cast<const _Float16*>(a.k);

@@ -26,6 +26,22 @@ struct LaunchArgs {
 // HIP runtime's status of the launch (0 = hipSuccess).
 int launch_forward(const LaunchArgs& a, void* stream);
 
+// The same forward, head_dim 64 only, built with one 32-row query block per
+// wave and 64-key tiles (launch_forward's head_dim 64 kernel takes two
+// blocks per wave and 32-key tiles).
+int launch_forward_d64_one_block(const LaunchArgs& a, void* stream);
+
+// Tile choice at head_dim 64, from the offline tile sweep on MI355X: the
+// one-block kernel for causal problems whose grid of two-block (256-row)
+// workgroups is below 2048 (fewer than four rounds of 512 co-resident
+// workgroups: the heaviest-first causal order then leaves the CUs unevenly
+// loaded at the end; one-block workgroups are twice as many), the two-block
+// kernel otherwise (it reads each K/V operand once for 64 query rows).
+constexpr int64_t kD64TwoBlockMinGrid = 2048;
+inline bool forward_d64_one_block(int64_t B, int64_t Hq, int64_t N, int causal) {
+  return causal && B * Hq * ((N + 255) / 256) < kD64TwoBlockMinGrid;
+}
+
 // Decode (KV cache) work plan: Nq new queries per query head against Nk
 // cached keys.  The G = Hq / Hkv query heads of a key/value head are packed
 // into rows r = g * Nq + i (row blocks of kDecodeRows); the keys are split

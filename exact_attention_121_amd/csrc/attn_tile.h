@@ -151,16 +151,16 @@ constexpr int wg_per_cu() {
   return hook ? hook : static_cast<int>(default_wg_per_cu(D));
 }
 // Workgroups per CU of the forward kernel: as above, except that without a
-// hook causal d = 256 takes two (a 76-byte spill per lane, but the second
-// wave per SIMD hides more of the causal kernel's latency: +3-5 % measured;
-// without the mask two are 5 % slower).  The decode kernel keeps one: its
-// split plan follows default_wg_per_cu.
+// hook d = 256 takes two (a 76-byte spill per lane, but the second wave per
+// SIMD hides more latency: +3-5 % measured with the mask; without it the
+// offline tile sweep measured +0.5 % at N = 2048 and +4.9 % at N = 8192).
+// The decode kernel keeps one: its split plan follows default_wg_per_cu.
 template <int D, bool CAUSAL>
 constexpr int fwd_wg_per_cu() {
   constexpr int hook = D == 32 ? ATTN_WG32 : D == 64 ? ATTN_WG64 : D == 96 ? ATTN_WG96 : D == 128 ? ATTN_WG128
                      : D == 160 ? ATTN_WG160 : D == 192 ? ATTN_WG192 : D == 224 ? ATTN_WG224 : ATTN_WG256;
   if (query_blocks<D>() != 1) return hook ? hook : 1;
-  return hook ? hook : (D == 256 && CAUSAL ? 2 : static_cast<int>(default_wg_per_cu(D)));
+  return hook ? hook : (D == 256 ? 2 : static_cast<int>(default_wg_per_cu(D)));
 }
 // Operands read ahead: a longer run of them pays only with the register
 // budget of one workgroup per CU.
@@ -670,8 +670,15 @@ __device__ __forceinline__ char* v_stage(char* smem, int st) { return smem + (2 
 
 // Calls f(std::integral_constant<int, D>{}) for a supported head_dim d
 // (a multiple of 32 from 32 to 256) and returns its status.
+// ATTN_ONLY_D: instantiate that head_dim alone (the second forward
+// translation unit, and the offline tile sweep's variants, which then
+// compile in seconds); any other d is refused.
 template <typename F>
 __host__ hipError_t with_head_dim(int d, F&& f) {
+#ifdef ATTN_ONLY_D
+  if (d != ATTN_ONLY_D) return hipErrorInvalidValue;
+  return f(std::integral_constant<int, ATTN_ONLY_D>{});
+#else
   switch (d) {
     case 32: return f(std::integral_constant<int, 32>{});
     case 64: return f(std::integral_constant<int, 64>{});
@@ -683,6 +690,7 @@ __host__ hipError_t with_head_dim(int d, F&& f) {
     case 256: return f(std::integral_constant<int, 256>{});
     default: return hipErrorInvalidValue;
   }
+#endif
 }
 
 // Instruction groups for the compiler's scheduler (masks of

@@ -4,26 +4,38 @@ The pages tie the block size to head_dim and the on-chip buffer ([CANN-FA]
 section "Key design points") and leave the best block size per sequence
 length to CANN's tuning engine ([FA-Infer] section 5, the item on AOE).
 This is the same idea for this kernel, offline: rebuild the forward kernel
-with other tile choices, check and time each on the GPU, and report the best
-per (head_dim, causal) case.
+with other tile choices, hold each to the fp64 oracle, time the accepted ones
+on the GPU at several sequence lengths, and report the best per (head_dim,
+causal, sequence length) case.
 
-    python -m exact_attention_121_amd.tile_sweep build    # compile the variants (no GPU needed)
-    python -m exact_attention_121_amd.tile_sweep run      # check and time them on cuda:0
-    (--dims 96,160 restricts either step to those head_dims)
+    python -m exact_attention_121_amd.tile_sweep build            # compile the variants (no GPU needed)
+    python tests/sweep_accept.py > gpurun_out/accepted.jsonl      # oracle check of every variant (GPU)
+    python -m exact_attention_121_amd.tile_sweep run --accepted gpurun_out/accepted.jsonl   # time them
+    (--dims 64,128 restricts any step to those head_dims)
 
-Choices swept (the compile-time hooks of csrc/attn_tile.h, per head_dim):
-keys per K/V tile (ATTN_BN*), matrix operands read ahead of their MFMA
-(ATTN_KAHEAD*) and, for head_dims above 128, workgroups per CU (ATTN_WG*:
-the register budget of 256 or 512 per lane).  (64-row waves, ATTN_QB* = 2, are left out: one wave per
-SIMD, 35-40 % slower where they fit, spilling where they do not.)  Only the
-forward translation unit is rebuilt; the decode and backward objects of the
-default build are linked unchanged (they keep the default tiles).
+Axes (compile-time hooks of csrc/attn_tile.h and csrc/attn_fwd_kernel.hip,
+per head_dim):
+  QB      32-row query blocks per wave (ATTN_QB*; 1 or 2: 128 or 256 query
+          rows per workgroup of 4 waves), at head_dims 64, 128, 256;
+  BN      keys per K/V tile (ATTN_BN*);
+  WG      workgroups per CU the kernel is compiled for (ATTN_WG*: the
+          register budget per lane);
+  KAHEAD  matrix operands read from LDS ahead of their MFMA (ATTN_KAHEAD*);
+  FORM    "pp": the 8-wave ping-pong kernel (two wave groups a phase apart,
+          operands read into registers a phase ahead; head_dim 128,
+          non-causal).
+Each variant compiles only its head_dim and fp16 (ATTN_ONLY_D), so a variant
+builds in seconds; it is linked with the default build's C-ABI object and
+stand-ins for the decode and backward launchers (variants serve attn_fwd
+only).
 
-A variant is accepted only if its output matches the default build's on the
-same inputs within max |dO| <= 1e-2 and |dLSE| <= 1e-3 (other tile sizes
-reorder the sums, so bitwise equality is not expected); the default build is
-the one the test suite holds to the oracle.  Results (JSON lines, one per
-variant and case, then the best per case) go to stdout.
+Acceptance is by the oracle, never by comparison with the default build:
+tests/sweep_accept.py (test infrastructure, the only code that may call the
+oracle) runs every built variant on validation problems of its head_dim
+(ragged N, GQA, spiky logits, causal and not) against the fp64 oracle at the
+parity bar, and `run` times only the variants it accepted.  Results (JSON
+lines: one per variant and case, the best per case, and the choice per
+(head_dim, causal) over the sequence lengths) go to stdout.
 """
 
 from __future__ import annotations
@@ -37,36 +49,66 @@ import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
-from .build import ARCH, CSRC, LIB_DIR, LIB_PATH, _hipcc, hip_flags
+from .build import ARCH, BUILD_DIR, CSRC, LIB_DIR, LIB_PATH, _hipcc, hip_flags
 
 SWEEP_DIR = os.path.join(LIB_DIR, "sweep")  # beside the library, so that the variants reach the GPU host
 
-# (head_dim, causal, B, H, N): the head_dim/causal combinations of the named
-# workloads at sizes that time in milliseconds, and the LLaMA-7B layer shape
-# (B=2, H=32, N=2048, non-causal) at the other head_dims.
-CASES = [(64, True, 8, 16, 4096), (128, False, 2, 32, 2048), (128, True, 1, 32, 8192), (256, True, 1, 32, 8192),
-         (32, False, 2, 32, 2048), (96, False, 2, 32, 2048), (160, False, 2, 32, 2048), (192, False, 2, 32, 2048),
-         (224, False, 2, 32, 2048)]
+
+def _v(qb=1, bn=64, wg=2, ka=4, form=""):
+    return dict(QB=qb, BN=bn, WG=wg, KAHEAD=ka, FORM=form)
+
 
 VARIANTS = {
-    32: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4)],
-    64: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
-    96: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
-    128: [dict(BN=bn, KAHEAD=ka) for bn in (32, 64, 128) for ka in (2, 4, 6)],
-    160: [dict(BN=bn, KAHEAD=ka, WG=wg) for bn in (32, 64) for ka in (4, 6, 8) for wg in (1, 2)],
-    192: [dict(BN=bn, KAHEAD=ka, WG=wg) for bn in (32, 64) for ka in (4, 6, 8) for wg in (1, 2)],
-    224: [dict(BN=bn, KAHEAD=ka, WG=wg) for bn in (32, 64) for ka in (4, 6, 8) for wg in (1, 2)],
-    256: [dict(BN=bn, KAHEAD=ka, WG=wg) for bn in (32, 64) for ka in (4, 6, 8) for wg in (1, 2)],
+    32: [_v(1, bn, 2, ka) for bn in (32, 64) for ka in (2, 4)],
+    64: [_v(qb, bn, wg, ka) for qb, bn, wg in ((1, 32, 2), (1, 64, 2), (1, 64, 3), (2, 32, 2), (2, 64, 1),
+                                               (2, 32, 1)) for ka in (2, 4)],
+    96: [_v(1, bn, 2, ka) for bn in (32, 64) for ka in (2, 4)],
+    128: [_v(qb, bn, wg, ka) for qb, bn, wg in ((1, 32, 2), (1, 64, 2), (1, 64, 1), (2, 32, 1))
+          for ka in (2, 4, 6)] + [_v(1, 32, 1, 4, "pp")],
+    160: [_v(1, bn, wg, ka) for bn, wg in ((32, 1), (32, 2), (64, 2)) for ka in (4, 6)],
+    192: [_v(1, bn, wg, ka) for bn, wg in ((32, 1), (32, 2), (64, 2)) for ka in (4, 6)],
+    224: [_v(1, bn, wg, ka) for bn, wg in ((32, 1), (32, 2), (64, 2)) for ka in (4, 6)],
+    256: [_v(1, bn, wg, ka) for bn, wg in ((32, 1), (32, 2), (64, 1)) for ka in (4, 6, 8)],
 }
-# The default build's choices (csrc/attn_launch.h default_key_tile and
-# default_wg_per_cu, csrc/attn_tile.h k_ahead).
-DEFAULT = {d: dict(BN=64 if d <= 128 else 32, KAHEAD=4 if d <= 224 else 6) for d in VARIANTS}
-for _d in (160, 192, 224, 256):
-    DEFAULT[_d]["WG"] = 2   # d = 256: the default of the causal kernel (the swept case); non-causal d = 256 takes 1
+QB_HOOK_DIMS = (64, 128, 256)   # head_dims with an ATTN_QB* hook
+
+# (head_dim, causal, N): every head_dim at the LLaMA-7B layer's N = 2048
+# non-causal; the head_dims of the named workloads (64, 128, 256) causal and
+# not at three or four sequence lengths.  H = Hkv = 32, B = max(1, 4096 / N)
+# so that every case has at least ~1 000 workgroups.
+CASES = ([(d, False, 2048) for d in (32, 96, 160, 192, 224)]
+         + [(64, c, n) for c in (False, True) for n in (1024, 4096, 16384)]
+         + [(128, c, n) for c in (False, True) for n in (1024, 2048, 8192)]
+         + [(256, c, n) for c in (False, True) for n in (2048, 8192)])
+
+
+def case_shape(d: int, causal: bool, N: int):
+    return max(1, 4096 // N), 32, N
 
 
 def variant_name(d: int, v: dict) -> str:
-    return f"d{d}_bn{v['BN']}_ka{v['KAHEAD']}" + (f"_wg{v['WG']}" if "WG" in v else "")
+    name = f"d{d}_qb{v['QB']}_bn{v['BN']}_wg{v['WG']}_ka{v['KAHEAD']}"
+    return name + (f"_{v['FORM']}" if v["FORM"] else "")
+
+
+def variant_flags(d: int, v: dict) -> list[str]:
+    flags = [f"-DATTN_ONLY_D={d}", "-DATTN_FP16_ONLY", f"-DATTN_BN{d}={v['BN']}", f"-DATTN_WG{d}={v['WG']}",
+             f"-DATTN_KAHEAD{d}={v['KAHEAD']}"]
+    if d in QB_HOOK_DIMS:
+        flags.append(f"-DATTN_QB{d}={v['QB']}")
+    elif v["QB"] != 1:
+        raise ValueError(f"no query-block hook at head_dim {d}")
+    if v["FORM"] == "pp":
+        flags.append("-DATTN_FWD_PP=1")
+    return flags
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(SWEEP_DIR, f"lib_{name}.so")
+
+
+def all_variants(dims=None):
+    return [(d, v, variant_name(d, v)) for d in VARIANTS if dims is None or d in dims for v in VARIANTS[d]]
 
 
 def _run(cmd):
@@ -75,44 +117,58 @@ def _run(cmd):
         raise RuntimeError(f"{' '.join(cmd)}\n{res.stderr[-2000:]}")
 
 
+# The variant libraries serve only attn_fwd: the decode and backward
+# launchers are replaced by stand-ins that refuse the launch, so that a
+# variant library holds one head_dim's forward kernels (~0.2 MB) instead of
+# the whole library, and the head_dim 64 tile choice of the C-ABI front end
+# is routed to the variant itself.
+_STUBS = """#include "attn_launch.h"
+namespace attn {
+// the variant itself at every head_dim 64 shape (no second tile choice)
+int launch_forward_d64_one_block(const LaunchArgs& a, void* s) { return launch_forward(a, s); }
+int launch_decode(const DecodeArgs&, void*) { return 1; }
+int launch_backward(const BwdArgs&, void*) { return 1; }
+int launch_backward_noalloc(const BwdArgs&, void*) { return 1; }
+}
+"""
+
+
 def build_variants(jobs: int = 8, dims=None) -> list[str]:
-    """Compile the default decode/backward/API objects once and one forward
-    object per variant; link one library per variant into lib/sweep/."""
+    """Compile one forward object per variant (its head_dim only) and link it
+    with the default build's C-ABI object and stand-ins for the decode and
+    backward launchers into lib/sweep/lib_<variant>.so."""
     os.makedirs(SWEEP_DIR, exist_ok=True)
     hipcc = _hipcc()
-    common = []
-    for src in ("attn_decode_kernel.hip", "attn_bwd_kernel.hip"):
-        obj = os.path.join(SWEEP_DIR, src + ".o")
-        _run([hipcc, *hip_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
-        common.append(obj)
-    api = os.path.join(SWEEP_DIR, "attn_api.cpp.o")
-    _run([hipcc, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-c", os.path.join(CSRC, "attn_api.cpp"), "-o", api])
-    common.append(api)
+    api = os.path.join(BUILD_DIR, "attn_api.cpp.o")
+    if not os.path.exists(api):
+        raise RuntimeError("build the library first (python -m exact_attention_121_amd.build)")
+    stub_src = os.path.join(SWEEP_DIR, "launch_stubs.cpp")
+    with open(stub_src, "w") as f:
+        f.write(_STUBS)
+    stub = os.path.join(SWEEP_DIR, "launch_stubs.o")
+    _run([hipcc, "-x", "c++", "-O2", "-std=c++17", "-fPIC", f"-I{CSRC}", "-c", stub_src, "-o", stub])
+    common = [api, stub]
 
     def one(item):
-        d, v = item
-        name = variant_name(d, v)
+        d, v, name = item
         obj = os.path.join(SWEEP_DIR, f"fwd_{name}.o")
-        lib = os.path.join(SWEEP_DIR, f"lib_{name}.so")
-        flags = [f"-DATTN_BN{d}={v['BN']}", f"-DATTN_KAHEAD{d}={v['KAHEAD']}"]
-        if "WG" in v:
-            flags.append(f"-DATTN_WG{d}={v['WG']}")
         try:
-            _run([hipcc, *hip_flags(flags), "-c", os.path.join(CSRC, "attn_fwd_kernel.hip"), "-o", obj])
-            _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, *common, "-o", lib])
+            _run([hipcc, *hip_flags(variant_flags(d, v)), "-c", os.path.join(CSRC, "attn_fwd_kernel.hip"), "-o",
+                  obj])
+            _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, *common, "-o", variant_path(name)])
+            os.remove(obj)
             return name, "built"
         except RuntimeError as e:
             return name, f"build failed: {str(e).splitlines()[-1][:200]}"
 
-    items = [(d, v) for d in VARIANTS if dims is None or d in dims for v in VARIANTS[d]]
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        out = list(ex.map(one, items))
+        out = list(ex.map(one, all_variants(dims)))
     for name, status in out:
         print(json.dumps({"variant": name, "status": status}), flush=True)
     return [n for n, st in out if st == "built"]
 
 
-def _load(path):
+def load_variant(path):
     lib = ctypes.CDLL(path)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, vp]
@@ -122,24 +178,28 @@ def _load(path):
 
 # Timing: the GPU is first kept busy for WARMUP_S seconds (its clock ramps up
 # over the first ~40 ms of load after idle, which would penalise whichever
-# variant ran first), then the case's variants are timed round-robin,
-# LAUNCHES launches per variant and round, the order reversed every other
-# round; the median over the rounds is reported.
+# variant ran first), then the case's variants and the default build are
+# timed round-robin, LAUNCHES launches per variant and round, the order
+# reversed every other round; the median over the rounds is reported.
 WARMUP_S = 0.3
 LAUNCHES = 10
+# A variant replaces the default for a case only when it is faster by more
+# than this (the spread of repeated timings of one build on one box).
+MARGIN = 0.02
 
 
-def run_sweep(repeats: int = 5, dims=None) -> None:
+def run_sweep(accepted: set, repeats: int = 5, dims=None) -> None:
     import time
 
     import torch
 
     dev = torch.device("cuda:0")
-    default = _load(LIB_PATH)
-    best = {}
-    for d, causal, B, H, N in CASES:
+    default = load_variant(LIB_PATH)
+    per_case = {}
+    for d, causal, N in CASES:
         if dims is not None and d not in dims:
             continue
+        B, H, _ = case_shape(d, causal, N)
         g = torch.Generator(device=dev)
         g.manual_seed(1000 + d + N)
         q = torch.randn(B, H, N, d, device=dev, generator=g).half()
@@ -156,55 +216,60 @@ def run_sweep(repeats: int = 5, dims=None) -> None:
             if st != 0:
                 raise RuntimeError(f"attn_fwd status {st}")
 
-        o_ref, l_ref = torch.empty_like(q), torch.empty(B, H, N, device=dev)
-        call(default, o_ref, l_ref)
-        torch.cuda.synchronize()
-        # Load and check every variant first.
-        ready = []
-        for vdef in VARIANTS[d]:
-            name = variant_name(d, vdef)
-            path = os.path.join(SWEEP_DIR, f"lib_{name}.so")
+        runs = [("default", default, {"variant": "default"})]
+        for dd, vdef, name in all_variants({d}):
             rec = {"case": case, "variant": name}
-            if not os.path.exists(path):
-                rec["status"] = "not built"
+            if name not in accepted:
+                rec["status"] = "not timed: not accepted by the oracle check"
                 print(json.dumps(rec), flush=True)
                 continue
-            lib = _load(path)
-            o, lse = torch.empty_like(q), torch.empty(B, H, N, device=dev)
-            call(lib, o, lse)
-            torch.cuda.synchronize()
-            dmax = (o.float() - o_ref.float()).abs().max().item()
-            lmax = (lse - l_ref).abs().max().item()
-            rec.update(max_abs_diff_O=dmax, max_abs_diff_LSE=lmax)
-            if not (dmax <= 1e-2 and lmax <= 1e-3):
-                rec["status"] = "rejected: output differs from the default build"
-                print(json.dumps(rec), flush=True)
-                continue
-            ready.append((vdef, name, lib, o, lse, rec))
+            if vdef["FORM"] == "pp" and causal:
+                continue  # the ping-pong form is built for the non-causal kernel only
+            runs.append((name, load_variant(variant_path(name)), rec))
+        bufs = {name: (torch.empty_like(q), torch.empty(B, H, N, device=dev)) for name, _, _ in runs}
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < WARMUP_S:
             for _ in range(5):
-                call(default, o_ref, l_ref)
+                call(default, *bufs["default"])
             torch.cuda.synchronize()
-        times = {name: [] for _, name, *_ in ready}
+        times = {name: [] for name, _, _ in runs}
         for r in range(repeats):
-            for vdef, name, lib, o, lse, rec in (ready if r % 2 == 0 else ready[::-1]):
+            for name, lib, _ in (runs if r % 2 == 0 else runs[::-1]):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 for _ in range(LAUNCHES):
-                    call(lib, o, lse)
+                    call(lib, *bufs[name])
                 e1.record(stream)
                 torch.cuda.synchronize()
                 times[name].append(e0.elapsed_time(e1) / LAUNCHES)
-        for vdef, name, lib, o, lse, rec in ready:
+        res = {}
+        for name, _, rec in runs:
             t = sorted(times[name])[len(times[name]) // 2]
-            rec.update(status="ok", median_ms=round(t, 4), tflops=round(flops / (t * 1e-3) / 1e12, 1),
-                       default=vdef == DEFAULT[d])
+            rec.update(case=case, status="ok", median_ms=round(t, 4), tflops=round(flops / (t * 1e-3) / 1e12, 1))
             print(json.dumps(rec), flush=True)
-            if case not in best or rec["tflops"] > best[case]["tflops"]:
-                best[case] = rec
-    for case, rec in best.items():
-        print(json.dumps({"best": case, "variant": rec["variant"], "tflops": rec["tflops"]}), flush=True)
+            res[name] = rec["tflops"]
+        best = max(res, key=res.get)
+        per_case[(d, causal, N)] = (best, res[best], res["default"])
+        print(json.dumps({"best": case, "variant": best, "tflops": res[best], "default_tflops": res["default"],
+                          "gain_over_default": round(res[best] / res["default"] - 1, 4)}), flush=True)
+    # The choice per (head_dim, causal): a variant that beats the default by
+    # more than MARGIN at some sequence lengths, or the default.
+    for (d, causal) in sorted({(d, c) for d, c, _ in per_case}):
+        rows = sorted((n, *per_case[(d, causal, n)]) for dd, c, n in per_case if (dd, c) == (d, causal))
+        pick = {n: (b if tf > df * (1 + MARGIN) else "default") for n, b, tf, df in rows}
+        print(json.dumps({"choice": f"d={d} causal={causal}", "per_N": pick}), flush=True)
+
+
+def read_accepted(path: str) -> set:
+    acc = set()
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                rec = json.loads(line)
+                if rec.get("accepted"):
+                    acc.add(rec["variant"])
+    return acc
 
 
 def main() -> int:
@@ -212,12 +277,17 @@ def main() -> int:
     ap.add_argument("what", choices=("build", "run"))
     ap.add_argument("--jobs", type=int, default=8)
     ap.add_argument("--dims", default="", help="comma-separated head_dims (default: all)")
+    ap.add_argument("--accepted", default="", help="JSON lines of tests/sweep_accept.py (run: required)")
     args = ap.parse_args()
     dims = {int(x) for x in args.dims.split(",")} if args.dims else None
     if args.what == "build":
         build_variants(args.jobs, dims)
     else:
-        run_sweep(dims=dims)
+        if not args.accepted:
+            print("run needs --accepted: variants are timed only after the oracle check "
+                  "(tests/sweep_accept.py)", file=sys.stderr)
+            return 2
+        run_sweep(read_accepted(args.accepted), dims=dims)
     return 0
 
 

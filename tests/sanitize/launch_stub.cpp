@@ -7,6 +7,7 @@
 
 namespace attn {
 int launch_forward(const LaunchArgs&, void*) { return 1; }
+int launch_forward_d64_one_block(const LaunchArgs&, void*) { return 1; }
 int launch_decode(const DecodeArgs&, void*) { return 1; }
 int launch_backward(const BwdArgs&, void*) { return 1; }
 int launch_backward_noalloc(const BwdArgs&, void*) { return 1; }

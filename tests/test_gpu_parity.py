@@ -95,3 +95,16 @@ def test_spiky_logits_small():
             o, lse = gpu_attention(q, k, v, scale, causal)
             O_ref, L_ref = attention_ref(q, k, v, scale, causal=causal)
             assert_parity(o, lse, O_ref, L_ref, what=f"spiky d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("B,H,N", [(64, 32, 256), (1, 8, 1000), (3, 4, 4096)])
+def test_d64_causal_both_tile_choices(B, H, N):
+    """head_dim 64 causal runs the two-block kernel on grids of at least 2048
+    two-block workgroups (B=64, H=32, N=256) and the one-block kernel below
+    (the other two shapes); every row against the oracle."""
+    _say(f"[parity] d=64 causal B={B} H={H} N={N}")
+    q, k, v = make_qkv(B, H, H, N, 64, seed=900 + N, spike_frac=0.01, spike_mult=8.0)
+    scale = float(np.float32(1.0 / 8.0))
+    o, lse = gpu_attention(q, k, v, scale, True)
+    O_ref, L_ref = attention_ref(q, k, v, scale, causal=True)
+    assert_parity(o, lse, O_ref, L_ref, what=f"d=64 causal B={B} H={H} N={N}")

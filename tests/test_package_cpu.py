@@ -27,10 +27,27 @@ def test_package_never_imports_the_oracle():
 def test_tile_sweep_table():
     from exact_attention_121_amd import tile_sweep as ts
     for d, variants in ts.VARIANTS.items():
-        assert ts.DEFAULT[d] in variants, f"default of d={d} is not swept"
         names = [ts.variant_name(d, v) for v in variants]
         assert len(set(names)) == len(names)
         row_chunks = 8 if d <= 64 else (16 if d <= 128 else 32)  # 16-byte chunks per (padded) LDS row
         for v in variants:
+            flags = ts.variant_flags(d, v)   # raises for a query-block count without a hook
+            assert f"-DATTN_ONLY_D={d}" in flags
             assert v["BN"] % 32 == 0 and v["BN"] * row_chunks % 256 == 0, "a tile must split evenly over 256 threads"
+            assert v["FORM"] in ("", "pp") and (v["FORM"] != "pp" or d == 128)
     assert {c[0] for c in ts.CASES} <= set(ts.VARIANTS)
+    for d, causal, N in ts.CASES:
+        B, H, n = ts.case_shape(d, causal, N)
+        assert n == N and B * H * (-(-N // 256)) >= 256, "every case fills the chip"
+
+
+def test_tile_sweep_run_needs_the_oracle_check(capsys):
+    from exact_attention_121_amd import tile_sweep as ts
+    import sys
+    argv = sys.argv
+    try:
+        sys.argv = ["tile_sweep", "run"]
+        assert ts.main() == 2
+    finally:
+        sys.argv = argv
+    assert "oracle check" in capsys.readouterr().err
