@@ -200,10 +200,33 @@ template <int D, bool CAUSAL, bool SUB, int NP, typename T>
 __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn_bwd_dkdv_kernel(BwdParams p, int k_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-key block per wave");
-  // Q stages 0/1, dO stages 0/1, then per stage the tile's LSE (log2) and
-  // Delta rows (64 floats each; a 32-row tile uses the first half).
-  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES + 2 * 2 * 64 * 4];
-  float* const rowterms = reinterpret_cast<float*>(smem + 4 * C::TILE_BYTES);  // [stage][lse2 | delta][64]
+  // The step loop is unrolled by two, so that the stage is a compile-time
+  // constant, above d = 64.  Up to d = 64 it is not: there the unrolled
+  // whole-tile form spills at two workgroups per CU (72 bytes per lane with
+  // the mask), and the unrolled sub-tile form measured 2 % slower.
+  constexpr bool kUnrolled = D > 64;
+  // Q stages 0/1, dO stages 0/1 and per stage the tile's LSE (log2) and
+  // Delta rows (64 floats each; a 32-row tile uses the first half), all
+  // filled by buffer-to-LDS copies.  Unrolled, each stage is an LDS object of
+  // its own: a read of an object that a copy in flight may write makes the
+  // compiler wait for every copy in flight, the next tile's included.  With a
+  // run-time stage index they are one object (selecting between objects at
+  // run time costs about 50 instructions a step).
+  constexpr int kRowTerms = 2 * 64 * 4;
+  constexpr int kFirst = kUnrolled ? C::TILE_BYTES : 4 * C::TILE_BYTES + 2 * kRowTerms;
+  constexpr int kOther = kUnrolled ? C::TILE_BYTES : 16;
+  __shared__ __attribute__((aligned(1024))) char qs0[kFirst];
+  __shared__ __attribute__((aligned(1024))) char qs1[kOther];
+  __shared__ __attribute__((aligned(1024))) char ds0[kOther];
+  __shared__ __attribute__((aligned(1024))) char ds1[kOther];
+  __shared__ __attribute__((aligned(16))) char rt0[kUnrolled ? kRowTerms : 16];
+  __shared__ __attribute__((aligned(16))) char rt1[kUnrolled ? kRowTerms : 16];
+  auto qst = [&](int i) -> char* { return kUnrolled ? (i == 0 ? qs0 : qs1) : qs0 + i * C::TILE_BYTES; };
+  auto dost = [&](int i) -> char* { return kUnrolled ? (i == 0 ? ds0 : ds1) : qs0 + (2 + i) * C::TILE_BYTES; };
+  // [lse2 | delta][64] of stage i
+  auto rts = [&](int i) -> float* {
+    return reinterpret_cast<float*>(kUnrolled ? (i == 0 ? rt0 : rt1) : qs0 + 4 * C::TILE_BYTES + i * kRowTerms);
+  };
 
   constexpr int NDT = C::DT / NP;       // 32-dim output tiles of this workgroup
   // Work list position -> (K/V head, key tile, dim part), contiguous per
@@ -264,7 +287,18 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
       }
   }
   auto voff = [&](int hi, int i) { return NP == 1 ? off.vofs(hi, i) : vpart[NP == 1 ? 0 : hi][NP == 1 ? 0 : i]; };
-  auto kofs = [&](int dc) { return off.kofs(dc); };
+  // Q / dO operand read offsets (chunks 2 dc + g of row lane % 32): with the
+  // XOR swizzle, swz(r, 2 dc + g) = kbase + 32 (dc ^ (f(r) >> 1)) (+256 for
+  // the upper 16 chunks of 32-chunk rows), kbase = (r CPR + (g ^ (f(r) & 1)))
+  // 16.  The step recomputes them from these two registers (two vector ops
+  // per read) instead of keeping Offsets' eight: at d = 128 the eight spilled,
+  // and every reload in the loop waited (vmcnt) for the next tile's copies.
+  const int fr = (swz<D>(lane & 31, 0) >> 4) - (lane & 31) * C::CPR;  // f(r)
+  int khalf = fr >> 1;
+  int kbase = ((lane & 31) * C::CPR + (g ^ (fr & 1))) * 16;
+  auto kofs = [&](int dc) {
+    return dc < 8 ? kbase + ((dc ^ khalf) << 5) : kbase + (((dc - 8) ^ khalf) << 5) + 256;
+  };
   LoadOffsets<D> lo;
   lo.init(tid);
 
@@ -284,8 +318,8 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
     const __amdgpu_buffer_rsrc_t drs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + qoff), (short)0, head_bytes, kBufferWord3);
     const uint32_t base = tile_base<D>(u < steps ? qt : 0, u < steps ? q_tiles : 0);
-    load_tile<D>(qrs, k_stage<D>(smem, st), base, lo, tid);
-    load_tile<D>(drs, v_stage<D>(smem, st), base, lo, tid);
+    load_tile<D>(qrs, qst(st), base, lo, tid);
+    load_tile<D>(drs, dost(st), base, lo, tid);
     // Waves 0 and 1 copy the tile's 64 LSE / Delta rows (4 bytes a lane);
     // rows past the head's padded rows read as 0 and are never used.
     if (wv < 2) {
@@ -294,8 +328,7 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
       const __amdgpu_buffer_rsrc_t rrs =
           __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.Npad * 4, kBufferWord3);
       const uint32_t voff = u < steps ? static_cast<uint32_t>(qt * C::BN + lane) * 4 : kSkipTile;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (lds_void*)(rowterms + (2 * st + wv) * 64), 4,
-                                               static_cast<int>(voff), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (lds_void*)(rts(st) + wv * 64), 4, static_cast<int>(voff), 0, 0, 0);
     }
   };
 
@@ -307,6 +340,8 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
   // stage addresses fold into the LDS instructions' offsets.
   auto step = [&](auto stc, int u) {
     const int st = stc;
+    // Keep the offset computation inside the loop (not hoisted and spilled).
+    if constexpr (SUB) asm volatile("" : "+v"(khalf), "+v"(kbase));
     const int gq = u / nq;
     const int q0 = (qt0 + (u - gq * nq)) * C::BN;
     // Causal: skip tiles whose every query precedes every key of the wave
@@ -315,8 +350,8 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
     issue(u + 1, st ^ 1);
     paranoid_sync();
     if (active) {
-      const float* lrow = rowterms + (2 * st) * 64;   // LSE (log2) of the tile's queries
-      const float* drow = rowterms + (2 * st + 1) * 64;   // Delta of the tile's queries
+      const float* lrow = rts(st);        // LSE (log2) of the tile's queries
+      const float* drow = rts(st) + 64;   // Delta of the tile's queries
       if constexpr (SUB) {
         // One 32-query sub-tile t at a time: S_t and dP_t, then P_t and
         // dS_t, then their products, so that only one sub-tile's scores and
@@ -328,12 +363,12 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
           // sub-tile t - 1, which lengthens register lifetimes (at d = 128
           // the spill falls from 52 to 36 bytes per lane; 4 % faster).
           __builtin_amdgcn_sched_barrier(0);
-          const f32x16 s = rows_times_frags<D, T>(k_stage<D>(smem, st), kf, kofs, t);   // S_t = Q_t K^T
-          const f32x16 dp = rows_times_frags<D, T>(v_stage<D>(smem, st), vf, kofs, t);  // dP_t = dO_t V^T
+          const f32x16 s = rows_times_frags<D, T>(qst(st), kf, kofs, t);   // S_t = Q_t K^T
+          const f32x16 dp = rows_times_frags<D, T>(dost(st), vf, kofs, t);  // dP_t = dO_t V^T
           half8 pf[2], dsf[2];
           p_ds_subtile<T>(s, dp, lrow + 32 * t + 4 * g, drow + 32 * t + 4 * g, p.c, pf, dsf);
-          tr_times_p<D, NDT, T>(v_stage<D>(smem, st), pf, voff, t, dv_acc);    // dV^T += dO_t^T P_t
-          tr_times_p<D, NDT, T>(k_stage<D>(smem, st), dsf, voff, t, dk_acc);   // dK^T += Q_t^T dS_t
+          tr_times_p<D, NDT, T>(dost(st), pf, voff, t, dv_acc);    // dV^T += dO_t^T P_t
+          tr_times_p<D, NDT, T>(qst(st), dsf, voff, t, dk_acc);   // dK^T += Q_t^T dS_t
         }
       } else {
         // The whole tile at once: S and dP of every sub-tile, the causal
@@ -356,8 +391,8 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
             delta[t][4 * rr + 3] = d4.w;
           }
         STile<D> s, dp;
-        qk_tile<D, T>(k_stage<D>(smem, st), kf, off, s);    // S = Q K^T: rows queries, columns keys
-        qk_tile<D, T>(v_stage<D>(smem, st), vf, off, dp);   // dP = dO V^T
+        qk_tile<D, T>(qst(st), kf, off, s);    // S = Q K^T: rows queries, columns keys
+        qk_tile<D, T>(dost(st), vf, off, dp);   // dP = dO V^T
 #pragma unroll
         for (int t = 0; t < C::NT; ++t)
 #pragma unroll
@@ -376,11 +411,11 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
         p_and_ds<D, T>(s, dp, delta, pf, dsf);
 #pragma unroll
         for (int t = 0; t < C::NT; ++t) {
-          tr_times_p<D, NDT, T>(v_stage<D>(smem, st), pf[0][t], voff, t, dv_acc);    // dV^T += dO^T P
+          tr_times_p<D, NDT, T>(dost(st), pf[0][t], voff, t, dv_acc);    // dV^T += dO^T P
         }
 #pragma unroll
         for (int t = 0; t < C::NT; ++t) {
-          tr_times_p<D, NDT, T>(k_stage<D>(smem, st), dsf[0][t], voff, t, dk_acc);   // dK^T += Q^T dS
+          tr_times_p<D, NDT, T>(qst(st), dsf[0][t], voff, t, dk_acc);   // dK^T += Q^T dS
         }
       }
     }
@@ -388,8 +423,7 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
     wait_vm_all();
     __syncthreads();
     };
-  if constexpr (bwd_dkdv_wg_per_cu<D, SUB>() == 2) {
-    // Unrolled, the step no longer fits two workgroups per CU.
+  if constexpr (!kUnrolled) {
     for (int u = 0; u < steps; ++u) step(u & 1, u);
   } else {
     for (int u = 0; u < steps; u += 2) {
@@ -400,7 +434,11 @@ __global__ __launch_bounds__(kThreads, (bwd_dkdv_wg_per_cu<D, SUB>())) void attn
 
   // The loop's last barrier freed the stages: each wave stages its rows of
   // dK and then dV there for coalesced stores.
-  char* region = row_region<D>(smem, wv);
+  constexpr int kRegion = 32 * C::CPR * 16;  // one wave's rows
+  constexpr int kPerStage = C::TILE_BYTES / kRegion;
+  static_assert(kPerStage >= 1 && 4 * kPerStage >= kWaves, "the output rows must fit the four stages");
+  const int obj = wv / kPerStage;
+  char* region = (obj < 2 ? qst(obj) : dost(obj - 2)) + (wv % kPerStage) * kRegion;
   store_rows<D, T, NDT>(region, dk_acc, p.scale, p.dk + kvoff + (size_t)kw0 * D + 32 * part * NDT, N - kw0, lane);
   store_rows<D, T, NDT>(region, dv_acc, 1.0f, p.dv + kvoff + (size_t)kw0 * D + 32 * part * NDT, N - kw0, lane);
 }

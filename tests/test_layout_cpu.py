@@ -195,3 +195,20 @@ def test_output_staging_round_trip(d):
     assert len(stores) == 32 * chunks
     # the four waves' regions fit the K/V stages (4 tiles of key_tile rows)
     assert 4 * region <= 4 * key_tile(d) * c * 16
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_k_operand_offsets_from_two_registers(d):
+    """The backward dK/dV kernel computes its Q/K operand read offsets in the
+    loop as kbase + 32 * (dc ^ (f(r) >> 1)) (+256 for the upper 16 chunks of
+    32-chunk rows), with kbase = (r * CPR + (g ^ (f(r) & 1))) * 16: the same
+    offsets as swz(r, 2 dc + g) for every lane and k-step."""
+    for lane in range(64):
+        r, g = lane & 31, lane >> 5
+        fr = f(d, r)
+        kbase = (r * cpr(d) + (g ^ (fr & 1))) * 16
+        for dc in range(d // 16):
+            lo = dc if dc < 8 else dc - 8
+            got = kbase + ((lo ^ (fr >> 1)) << 5) + (256 if dc >= 8 else 0)
+            assert got == swz(d, r, 2 * dc + g), (d, lane, dc)
+
