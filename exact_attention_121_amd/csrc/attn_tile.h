@@ -495,9 +495,56 @@ __device__ __forceinline__ void softmax_tile(const STile<D>& s, float c, const f
 
 // Adds the sum of the fp16 probabilities (exactly the values multiplied
 // into V) to the lane's partial row sums l.
+//
+// v_dot2 does not overlap the matrix instructions on gfx950 (about 4 cycles
+// each of the matrix pipe's time, measured), while packed fp16 additions
+// mostly do.  At d = 256 the lane's adjacent probabilities are therefore
+// first added in pairs in fp16 (one rounding of a sum of two values, a
+// relative 2^-11 at most), halving the v_dot2 count: +3 to +6 % on MI355X,
+// and at most 4e-4 of LSE error against the fp64 oracle in the tests'
+// problems (1.9e-4 before).  At d = 64 and 128 it gained under 1 %, and two
+// or more fp16 levels cost more accuracy (1.3e-3 of LSE error with the whole
+// tree at d = 64 with spiky logits), so the other head_dims keep v_dot2.
+#ifndef ATTN_ROWSUM_PK
+#define ATTN_ROWSUM_PK -1  // fp16 pair levels; -1: one at d = 256, none elsewhere
+#endif
+template <int D>
+constexpr int row_sum_fp16_levels() { return ATTN_ROWSUM_PK >= 0 ? ATTN_ROWSUM_PK : (D == 256 ? 1 : 0); }
+
 template <int D, typename T = _Float16>
 __device__ __forceinline__ void add_row_sums(const PTile<D>& pf, float (&l_run)[Cfg<D>::QB]) {
   using C = Cfg<D>;
+  constexpr int kLevels = row_sum_fp16_levels<D>();
+  if constexpr (kLevels > 0 && !std::is_same_v<T, __bf16>) {
+    // kLevels levels of a pairwise tree of packed fp16 additions over the
+    // tile's 8 NT pairs, then v_dot2 into fp32.
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      constexpr int n = 8 * C::NT;
+      half2v v[n];
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[8 * t + 4 * h + i] = half2v{pf[qb][t][h][2 * i], pf[qb][t][h][2 * i + 1]};
+      int w = n;
+#pragma unroll
+      for (int lvl = 0; lvl < kLevels && w > 1; ++lvl) {
+        w /= 2;
+#pragma unroll
+        for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+      }
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < w; ++i) {
+        if (i & 1) l1 = __builtin_amdgcn_fdot2(v[i], half2v{1.0f16, 1.0f16}, l1, false);
+        else l0 = __builtin_amdgcn_fdot2(v[i], half2v{1.0f16, 1.0f16}, l0, false);
+      }
+      l_run[qb] += l0 + l1;
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     float l0 = 0.f, l1 = 0.f;
