@@ -6,9 +6,14 @@
 Every run first runs untimed steps for 0.3 s (the GPU clock ramps up over
 the first ~40 ms of load; the line reports this as "clock_warmup"), then the
 --warmup steps (default 10), then times --steps steps (default: about 0.25 s
-of them); the JSON line reports the counts used, the kernel time per step
-(mean, median, min from HIP events around every step) and the mean graphics
-clock over the timed steps.
+of them); the JSON line reports the counts used and the kernel time per step
+(mean, median, min from HIP events around every step).  The forward and
+backward lines also carry "gemm_reference": the rate of a plain fp16 GEMM
+(torch.matmul, i.e. hipBLASLt) measured right after the timed steps on the
+same GPU, the practical matrix-core ceiling under the chip's power limit;
+and "sclk": the shader clock and matrix-core busy fraction that rocprofv3
+counters measured for the same kernel code (the committed counter summary,
+keyed by a hash of the kernel sources; null once the code has changed).
 
 A step is one call of the whole hot path (one fused forward kernel) over one
 batch of synthetic fp16 inputs already resident in device memory.  The default
@@ -74,76 +79,56 @@ TIMED_S = 0.25
 DEFAULT_WARMUP = 10
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock (MHz) from the driver's metrics table
-    (amdsmi) in a background thread while the timed steps run; reports None
-    where the metrics cannot be read."""
+def gemm_reference(dev, n: int = 8192, seconds: float = 0.5) -> dict:
+    """TFLOP/s of a plain n x n x n fp16 GEMM (torch.matmul, which dispatches
+    to hipBLASLt) on the same GPU: warmed up for `seconds`, then timed with
+    HIP events.  A measured ceiling for dense fp16 matrix work on this chip
+    at the clock its power limit allows, next to the published peak."""
+    import torch
 
-    def __init__(self, period_s: float = 0.002):
-        self.period_s = period_s
-        self.samples = []
-        self.error = None
-        self._stop = None
-        self._thread = None
-        self._handle = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self._amdsmi = amdsmi
-            handles = amdsmi.amdsmi_get_processor_handles()
-            self._handle = handles[0] if handles else None
-            if self._handle is not None and self._read() is None:
-                self._handle = None
-                self.error = "no graphics clock in the metrics table"
-        except Exception as e:  # no driver access: the figure is reported as null
-            self.error = f"{type(e).__name__}: {e}"
+    a = torch.randn(n, n, device=dev, dtype=torch.float16)
+    b = torch.randn(n, n, device=dev, dtype=torch.float16)
+    c = torch.empty(n, n, device=dev, dtype=torch.float16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
+            "shape": f"{n}x{n}x{n} fp16, fp32 accumulate", "library": "torch.matmul (hipBLASLt)",
+            "ms": round(ms, 4)}
 
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
-        vals = []
-        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
-            x = m.get(key)
-            xs = x if isinstance(x, (list, tuple)) else [x]
-            vals = [float(v) for v in xs if isinstance(v, (int, float)) and 0 < v < 10000]
-            if vals:
-                return sum(vals) / len(vals)
+
+def counter_clock(workload_name: str, path=TRAFFIC_FILE, sources=FORWARD_SOURCES):
+    """Shader clock and matrix-core busy fraction of the dominant kernel from
+    the committed rocprofv3 counter record (GRBM_GUI_ACTIVE over the kernel's
+    duration; SQ_VALU_MFMA_BUSY_CYCLES over cycles x 1024 SIMDs), or None
+    when there is none for this workload or the kernel changed since."""
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
         return None
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                v = self._read()
-                if v is not None:
-                    self.samples.append(v)
-            except Exception as e:
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period_s)
-
-    def start(self):
-        import threading
-        if self._handle is None:
-            return
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-        self._thread.start()
-
-    def stop(self):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-        if not self.samples:
-            return {"mean_mhz": None, "samples": 0, "source": "amdsmi gpu_metrics", "error": self.error}
-        xs = sorted(self.samples)
-        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": xs[0], "max_mhz": xs[-1],
-                "samples": len(xs), "source": "amdsmi gpu_metrics (current graphics clock, every ~2 ms)"}
+    entry = rec.get(workload_name)
+    if not entry or entry.get("kernel_code_sha256_16") != kernel_source_hash(sources) or "clock_mhz" not in entry:
+        return None
+    return {"mhz": entry["clock_mhz"], "mfma_busy": entry.get("mfma_busy"),
+            "source": "rocprofv3 counters of the same kernel code (" + entry.get("mfma_summary", "") + ")"}
 
 
 def run_timed(step, args, dev):
     """Runs the clock warm-up, the requested warm-up steps and the timed
     steps of `step(i)`; sets args.warmup and args.steps to the counts used.
-    Returns (wall ms per step, kernel-time stats, clock-warm-up record, SCLK
-    record).  The timed steps are bracketed by one pair of HIP events on the
+    Returns (wall ms per step, kernel-time stats, clock-warm-up record).  The timed steps are bracketed by one pair of HIP events on the
     launch stream (their mean is the region's time over the steps; it agrees
     with a rocprofv3 kernel trace of the same dispatches).  Median, min and
     max come from a second pass of as many steps right after it with events
@@ -177,9 +162,7 @@ def run_timed(step, args, dev):
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    clock = ClockSampler()
     torch.cuda.synchronize()
-    clock.start()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
@@ -187,7 +170,6 @@ def run_timed(step, args, dev):
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    sclk = clock.stop()
     n += args.steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for i in range(args.steps):
@@ -198,7 +180,7 @@ def run_timed(step, args, dev):
     per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     stats = {"mean": ev0.elapsed_time(ev1) / args.steps, "median": per[len(per) // 2], "min": per[0],
              "max": per[-1], "mean_per_step_events": sum(per) / len(per)}
-    return (t1 - t0) * 1e3 / args.steps, stats, ramp, sclk
+    return (t1 - t0) * 1e3 / args.steps, stats, ramp
 
 
 def host_cpu_model() -> str:
@@ -408,7 +390,7 @@ def run_decode(args) -> int:
         kc, vc = kvs[i % copies]
         ea.attn_decode(q, kc, vc, scale=w.scale, causal=w.causal, out=o, lse=lse, workspace=ws)
 
-    ms_per_step, stats, ramp, sclk = run_timed(step, args, dev)
+    ms_per_step, stats, ramp = run_timed(step, args, dev)
     avg_step_ms = stats["mean"]
     value = w.hbm_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = w.hbm_bytes / (avg_step_ms * 1e-3) / 1e9
@@ -435,7 +417,7 @@ def run_decode(args) -> int:
                      "scope": "whole step: per-chunk kernel plus merge kernel"},
         "kernel_ms": kernel_ms_record(stats, args.steps, "one or two kernels per step"),
         "clock_warmup": ramp,
-        "sclk": sclk,
+        "sclk": counter_clock(w.name, DECODE_TRAFFIC_FILE, DECODE_SOURCES),
         "kernel_code_sha256_16": kernel_source_hash(DECODE_SOURCES),
     }
     if args.calibrate_copy_mib > 0:
@@ -525,7 +507,7 @@ def run_backward(args) -> int:
     def step(_i):
         ea.attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    ms_per_step, stats, ramp, sclk = run_timed(step, args, dev)
+    ms_per_step, stats, ramp = run_timed(step, args, dev)
     avg_step_ms = stats["mean"]
     flops = 10 * w.d * w.pairs
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -555,9 +537,13 @@ def run_backward(args) -> int:
                      "scope": "whole step: dQ (with the row terms) and dK/dV kernels; 10 d FLOPs per visible pair"},
         "kernel_ms": kernel_ms_record(stats, args.steps, "two kernels per step"),
         "clock_warmup": ramp,
-        "sclk": sclk,
+        "sclk": None if bf16 else counter_clock(w.name, BACKWARD_TRAFFIC_FILE, BACKWARD_SOURCES),
         "kernel_code_sha256_16": kernel_source_hash(BACKWARD_SOURCES),
     }
+    if not args.no_gemm_reference:
+        g = gemm_reference(dev)
+        g["attention_over_gemm"] = round(value / g["tflops"], 4)
+        result["gemm_reference"] = g
     if args.calibrate_copy_mib > 0:
         result["copy_calibration"] = calibration_copy(args.calibrate_copy_mib, dev)
     if not args.no_cpu_baseline:
@@ -595,6 +581,8 @@ def main() -> int:
                     help="also run a plain elementwise copy of this many MiB (fp16 -> fp16, "
                          "y = -x) three times, so that hardware byte counters can be "
                          "calibrated against a kernel of known traffic")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the fp16 GEMM reference measured after the timed steps")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -630,7 +618,7 @@ def main() -> int:
     def step(_i):
         ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
 
-    ms_per_step, stats, ramp, sclk = run_timed(step, args, dev)
+    ms_per_step, stats, ramp = run_timed(step, args, dev)
     avg_kernel_ms = stats["mean"]
 
     value = w.flops / (ms_per_step * 1e-3) / 1e12
@@ -659,9 +647,13 @@ def main() -> int:
                      "traffic": traffic if args.dtype == "f16" else None},
         "kernel_ms": kernel_ms_record(stats, args.steps, "one kernel per step"),
         "clock_warmup": ramp,
-        "sclk": sclk,
+        "sclk": counter_clock(w.name) if args.dtype == "f16" else None,
         "kernel_code_sha256_16": kernel_source_hash(),
     }
+    if not args.no_gemm_reference:
+        g = gemm_reference(dev)
+        g["attention_over_gemm"] = round(value / g["tflops"], 4)
+        result["gemm_reference"] = g
     if args.calibrate_copy_mib > 0:
         result["copy_calibration"] = calibration_copy(args.calibrate_copy_mib, dev)
     if not args.no_cpu_baseline:
