@@ -11,9 +11,11 @@ of them); the JSON line reports the counts used and the kernel time per step
 backward lines also carry "gemm_reference": the rate of a plain fp16 GEMM
 (torch.matmul, i.e. hipBLASLt) measured right after the timed steps on the
 same GPU, the practical matrix-core ceiling under the chip's power limit;
-and "sclk": the shader clock and matrix-core busy fraction that rocprofv3
-counters measured for the same kernel code (the committed counter summary,
-keyed by a hash of the kernel sources; null once the code has changed).
+and "sclk": the shader clock measured live by a one-wave probe on a second
+stream during a repeat of the timed steps ("live"), and the clock and
+matrix-core busy fraction that rocprofv3 counters measured for the same kernel
+code ("counters": the committed counter summary, keyed by a hash of the
+kernel sources; null once the code has changed).
 
 A step is one call of the whole hot path (one fused forward kernel) over one
 batch of synthetic fp16 inputs already resident in device memory.  The default
@@ -101,11 +103,70 @@ def gemm_reference(dev, n: int = 8192, seconds: float = 0.5) -> dict:
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    # The same again with the clock probe beside it (not timed).
+    probe = ClockProbe(dev)
+    torch.cuda.synchronize()
+    probe.start(0.6 * ms * reps)
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
     tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
     del a, b, c
     return {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
             "shape": f"{n}x{n}x{n} fp16, fp32 accumulate", "library": "torch.matmul (hipBLASLt)",
-            "ms": round(ms, 4)}
+            "ms": round(ms, 4), "sclk_live_mhz": probe.result()["mhz"]}
+
+
+class ClockProbe:
+    """Mean shader clock of one CU under the timed kernels' load: a one-wave
+    kernel (exact_attention_121_amd/csrc/sclk_probe.hip, its own small
+    library) on a second stream of default priority counts shader-clock
+    cycles against the constant-rate wall counter over a window of the
+    per-step-event pass, which repeats the timed steps (so the timed pass
+    itself runs unperturbed)."""
+
+    def __init__(self, dev):
+        import ctypes
+
+        import torch
+
+        from exact_attention_121_amd.build import PROBE_PATH
+
+        self.lib, self.error, self.khz = None, None, 0
+        try:
+            lib = ctypes.CDLL(PROBE_PATH)
+            lib.attn_sclk_probe.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_void_p]
+            lib.attn_sclk_probe.restype = ctypes.c_int
+            lib.attn_wall_clock_khz.restype = ctypes.c_int
+            self.khz = lib.attn_wall_clock_khz()
+            if self.khz <= 0:
+                raise OSError("no wall clock rate")
+            self.lib = lib
+        except OSError as e:
+            self.error = f"probe library not usable: {e}"
+        self.out = torch.zeros(2, dtype=torch.int64, device=dev)
+        self.stream = torch.cuda.Stream(device=dev)
+        self.window_ms = 0.0
+
+    def start(self, window_ms: float):
+        """Queue the probe (call before queuing the kernels it should see)."""
+        if self.lib is None:
+            return
+        self.window_ms = max(0.2, min(window_ms, 2000.0))
+        if self.lib.attn_sclk_probe(self.out.data_ptr(), int(self.khz * self.window_ms), self.stream.cuda_stream):
+            self.error, self.lib = "probe launch failed", None
+
+    def result(self) -> dict:
+        """Call after a device synchronisation."""
+        rec = {"source": "shader-clock cycles / wall-clock ticks of a one-wave probe on a second stream during the "
+                         "per-step-event pass (one CU)"}
+        if self.lib is None:
+            rec.update(mhz=None, error=self.error)
+            return rec
+        cycles, ticks = (int(x) for x in self.out.tolist())
+        rec.update(mhz=round(cycles / (ticks / (self.khz * 1e3)) / 1e6, 1) if ticks > 0 else None,
+                   window_ms=round(ticks / self.khz, 3))
+        return rec
 
 
 def counter_clock(workload_name: str, path=TRAFFIC_FILE, sources=FORWARD_SOURCES):
@@ -128,7 +189,8 @@ def counter_clock(workload_name: str, path=TRAFFIC_FILE, sources=FORWARD_SOURCES
 def run_timed(step, args, dev):
     """Runs the clock warm-up, the requested warm-up steps and the timed
     steps of `step(i)`; sets args.warmup and args.steps to the counts used.
-    Returns (wall ms per step, kernel-time stats, clock-warm-up record).  The timed steps are bracketed by one pair of HIP events on the
+    Returns (wall ms per step, kernel-time stats, clock-warm-up record, live
+    shader-clock record).  The timed steps are bracketed by one pair of HIP events on the
     launch stream (their mean is the region's time over the steps; it agrees
     with a rocprofv3 kernel trace of the same dispatches).  Median, min and
     max come from a second pass of as many steps right after it with events
@@ -172,6 +234,9 @@ def run_timed(step, args, dev):
     t1 = time.perf_counter()
     n += args.steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    probe = ClockProbe(dev)
+    torch.cuda.synchronize()
+    probe.start(0.6 * (t1 - t0) * 1e3)
     for i in range(args.steps):
         evs[i].record(stream)
         step(n + i)
@@ -180,7 +245,7 @@ def run_timed(step, args, dev):
     per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     stats = {"mean": ev0.elapsed_time(ev1) / args.steps, "median": per[len(per) // 2], "min": per[0],
              "max": per[-1], "mean_per_step_events": sum(per) / len(per)}
-    return (t1 - t0) * 1e3 / args.steps, stats, ramp
+    return (t1 - t0) * 1e3 / args.steps, stats, ramp, probe.result()
 
 
 def host_cpu_model() -> str:
@@ -390,7 +455,7 @@ def run_decode(args) -> int:
         kc, vc = kvs[i % copies]
         ea.attn_decode(q, kc, vc, scale=w.scale, causal=w.causal, out=o, lse=lse, workspace=ws)
 
-    ms_per_step, stats, ramp = run_timed(step, args, dev)
+    ms_per_step, stats, ramp, live_clock = run_timed(step, args, dev)
     avg_step_ms = stats["mean"]
     value = w.hbm_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = w.hbm_bytes / (avg_step_ms * 1e-3) / 1e9
@@ -417,7 +482,7 @@ def run_decode(args) -> int:
                      "scope": "whole step: per-chunk kernel plus merge kernel"},
         "kernel_ms": kernel_ms_record(stats, args.steps, "one or two kernels per step"),
         "clock_warmup": ramp,
-        "sclk": counter_clock(w.name, DECODE_TRAFFIC_FILE, DECODE_SOURCES),
+        "sclk": {"live": live_clock, "counters": counter_clock(w.name, DECODE_TRAFFIC_FILE, DECODE_SOURCES)},
         "kernel_code_sha256_16": kernel_source_hash(DECODE_SOURCES),
     }
     if args.calibrate_copy_mib > 0:
@@ -507,7 +572,7 @@ def run_backward(args) -> int:
     def step(_i):
         ea.attn_bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    ms_per_step, stats, ramp = run_timed(step, args, dev)
+    ms_per_step, stats, ramp, live_clock = run_timed(step, args, dev)
     avg_step_ms = stats["mean"]
     flops = 10 * w.d * w.pairs
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -537,7 +602,8 @@ def run_backward(args) -> int:
                      "scope": "whole step: dQ (with the row terms) and dK/dV kernels; 10 d FLOPs per visible pair"},
         "kernel_ms": kernel_ms_record(stats, args.steps, "two kernels per step"),
         "clock_warmup": ramp,
-        "sclk": None if bf16 else counter_clock(w.name, BACKWARD_TRAFFIC_FILE, BACKWARD_SOURCES),
+        "sclk": {"live": live_clock,
+                 "counters": None if bf16 else counter_clock(w.name, BACKWARD_TRAFFIC_FILE, BACKWARD_SOURCES)},
         "kernel_code_sha256_16": kernel_source_hash(BACKWARD_SOURCES),
     }
     if not args.no_gemm_reference:
@@ -618,7 +684,7 @@ def main() -> int:
     def step(_i):
         ea.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
 
-    ms_per_step, stats, ramp = run_timed(step, args, dev)
+    ms_per_step, stats, ramp, live_clock = run_timed(step, args, dev)
     avg_kernel_ms = stats["mean"]
 
     value = w.flops / (ms_per_step * 1e-3) / 1e12
@@ -647,7 +713,7 @@ def main() -> int:
                      "traffic": traffic if args.dtype == "f16" else None},
         "kernel_ms": kernel_ms_record(stats, args.steps, "one kernel per step"),
         "clock_warmup": ramp,
-        "sclk": counter_clock(w.name) if args.dtype == "f16" else None,
+        "sclk": {"live": live_clock, "counters": counter_clock(w.name) if args.dtype == "f16" else None},
         "kernel_code_sha256_16": kernel_source_hash(),
     }
     if not args.no_gemm_reference:

@@ -20,7 +20,8 @@ build or to the oracle:
 * ``pp``: the 8-wave ping-pong form of the head_dim 128 non-causal forward
   (two wave groups a phase apart, operands staged in registers a phase
   ahead), measured slower than the default on gfx950;
-the GPU tests hold the last two to the oracle.
+the GPU tests hold the last two to the oracle.  It also builds
+``lib/libattn_probe.so``, the benchmark's shader-clock probe (sclk_probe.hip).
 
 The sources compile in parallel (one hipcc per source and variant).
 """
@@ -56,6 +57,12 @@ VARIANTS = {
     # the 8-wave ping-pong kernel for the head_dim 128 non-causal forward
     "pp": (["-DATTN_FWD_PP=1"], ["attn_fwd_kernel.hip"]),
 }
+
+
+# The benchmark's shader-clock probe: its own small library, not part of the
+# attention path (bench.py loads it; nothing in the package does).
+PROBE_SOURCE = "sclk_probe.hip"
+PROBE_PATH = os.path.join(LIB_DIR, "libattn_probe.so")
 
 
 def variant_path(name: str) -> str:
@@ -110,7 +117,9 @@ def build(verbose: bool = False, extra_flags=(), variants=True) -> str:
         compiles.append([hipcc, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c",
                          os.path.join(CSRC, src), "-o", obj])
         default_objs[src] = obj
-    links = [(LIB_PATH, [default_objs[s] for s in HIP_SOURCES + CXX_SOURCES])]
+    probe_obj = os.path.join(BUILD_DIR, PROBE_SOURCE + ".o")
+    compiles.append([hipcc, *hip_flags(extra_flags), "-c", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_obj])
+    links = [(LIB_PATH, [default_objs[s] for s in HIP_SOURCES + CXX_SOURCES]), (PROBE_PATH, [probe_obj])]
     if variants:
         os.makedirs(VARIANT_DIR, exist_ok=True)
         for name, (flags, changed) in VARIANTS.items():

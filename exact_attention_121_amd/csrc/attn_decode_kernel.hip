@@ -43,7 +43,11 @@ template <int D, bool CAUSAL, typename T, int WGS>
 __global__ __launch_bounds__(kThreads, WGS) void attn_decode_split_kernel(DecParams p) {
   using C = Cfg<D>;
   static_assert(C::QB == 1 && C::BM == kDecodeRows, "decode packs 128 rows per workgroup, 32 per wave");
+  // K stages 0/1 then V stages 0/1 in one array.  (As separate objects,
+  // which spares the forward its waits for copies in flight before the V
+  // operand reads, the decode steps measured 0.4 % faster to 1.4 % slower.)
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
+  const KVStages<D> st{{smem, smem + C::TILE_BYTES}, {smem + 2 * C::TILE_BYTES, smem + 3 * C::TILE_BYTES}};
 
   const int split = blockIdx.x % p.splits;
   const int grp = blockIdx.x / p.splits;  // (b * Hkv + kvh) * row_blocks + rb
@@ -84,9 +88,9 @@ __global__ __launch_bounds__(kThreads, WGS) void attn_decode_split_kernel(DecPar
 
   LoadOffsets<D> lo;
   lo.init(tid);
-  load_tile<D>(krs, k_stage<D>(smem, 0), tile_base<D>(t0, t1), lo, tid);
-  load_tile<D>(vrs, v_stage<D>(smem, 0), tile_base<D>(t0, t1), lo, tid);
-  load_tile<D>(krs, k_stage<D>(smem, 1), tile_base<D>(t0 + 1, t1), lo, tid);
+  load_tile<D>(krs, st.k[0], tile_base<D>(t0, t1), lo, tid);
+  load_tile<D>(vrs, st.v[0], tile_base<D>(t0, t1), lo, tid);
+  load_tile<D>(krs, st.k[1], tile_base<D>(t0 + 1, t1), lo, tid);
 
   const _Float16* __restrict__ qrow_ptr = p.q + (((size_t)b * p.Hq + hq) * Nq + iq) * D;
 #pragma unroll
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kThreads, WGS) void attn_decode_split_kernel(DecPar
   STile<D> sa, sb;
   if (w.nt_w > t0) {
     const int kv0 = t0 * C::BN;
-    qk_tile<D, T>(k_stage<D>(smem, 0), w.qf, w.off, sa);
+    qk_tile<D, T>(st.k[0], w.qf, w.off, sa);
     if (kv0 + C::BN > Nk || (CAUSAL && kv0 + C::BN - 1 > w.qw0)) mask_tile<D, CAUSAL>(sa, kv0, Nk, w.qrow, w.g);
     tile_max<D>(sa, w.c, w.m_run);
     // A row that sees no key of this chunk (causal: the chunk starts after
@@ -117,8 +121,8 @@ __global__ __launch_bounds__(kThreads, WGS) void attn_decode_split_kernel(DecPar
   __syncthreads();
 
   for (int j = t0; j < t1; j += 2) {
-    pipeline_step<D, CAUSAL, 0, T>(j, t1, smem, krs, vrs, lo, tid, w, sa, sb);
-    if (j + 1 < t1) pipeline_step<D, CAUSAL, 1, T>(j + 1, t1, smem, krs, vrs, lo, tid, w, sb, sa);
+    pipeline_step<D, CAUSAL, 0, T>(j, t1, st, krs, vrs, lo, tid, w, sa, sb);
+    if (j + 1 < t1) pipeline_step<D, CAUSAL, 1, T>(j + 1, t1, st, krs, vrs, lo, tid, w, sb, sa);
   }
 
   // Partial result of this chunk for the rows that exist: O_s = O^T / l_s

@@ -103,8 +103,12 @@ struct Params {
 template <int D, bool CAUSAL, typename T>
 __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_fwd_kernel(Params p) {
   using C = Cfg<D>;
-  // K stages 0/1 then V stages 0/1.
-  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
+  // K stages 0/1 and V stages 0/1, each an LDS object of its own.
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
+  const KVStages<D> st{{k0s, k1s}, {v0s, v1s}};
 
   // Work list position -> (batch*head, query tile), contiguous per XCD;
   // causal: heaviest tiles first across a group of heads.
@@ -160,9 +164,9 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
 
   LoadOffsets<D> lo;
   lo.init(tid);
-  load_tile<D>(krs, k_stage<D>(smem, 0), 0, lo, tid);
-  load_tile<D>(vrs, v_stage<D>(smem, 0), 0, lo, tid);
-  load_tile<D>(krs, k_stage<D>(smem, 1), tile_base<D>(1, nt), lo, tid);
+  load_tile<D>(krs, st.k[0], 0, lo, tid);
+  load_tile<D>(vrs, st.v[0], 0, lo, tid);
+  load_tile<D>(krs, st.k[1], tile_base<D>(1, nt), lo, tid);
 
   // Q fragments (B operand of S^T): dims 16*dc + 8*g .. +7 of each row.
 #pragma unroll
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
   // Prologue: logits of tile 0 and the first running max.
   STile<D> sa, sb;
   if (w.nt_w > 0) {
-    qk_tile<D, T>(k_stage<D>(smem, 0), w.qf, w.off, sa);
+    qk_tile<D, T>(st.k[0], w.qf, w.off, sa);
     if (C::BN > N || (CAUSAL && C::BN - 1 > w.qw0)) mask_tile<D, CAUSAL>(sa, 0, N, w.qrow, w.g);
     // Key 0 is visible to every row, so these maxima are finite.
     tile_max<D>(sa, w.c, w.m_run);
@@ -200,14 +204,14 @@ __global__ __launch_bounds__(kThreads, (fwd_wg_per_cu<D, CAUSAL>())) void attn_f
   // pipeline is scheduled better when it is told so.
   constexpr bool kUniform = !CAUSAL && D == 64;
   for (int j = 0; j < nt; j += 2) {
-    pipeline_step<D, CAUSAL, 0, T, kUniform>(j, nt, smem, krs, vrs, lo, tid, w, sa, sb);
-    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1, T, kUniform>(j + 1, nt, smem, krs, vrs, lo, tid, w, sb, sa);
+    pipeline_step<D, CAUSAL, 0, T, kUniform>(j, nt, st, krs, vrs, lo, tid, w, sa, sb);
+    if (j + 1 < nt) pipeline_step<D, CAUSAL, 1, T, kUniform>(j + 1, nt, st, krs, vrs, lo, tid, w, sb, sa);
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).  After the loop's last
   // barrier no copy or read uses the K/V stages any more, so each wave
   // stages its rows for a coalesced store in an LDS region of its own.
-  char* region = row_region<D>(smem, wv);
+  char* region = st.region(wv);
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     const int row = w.qrow + 32 * qb;

@@ -715,6 +715,28 @@ __device__ __forceinline__ char* k_stage(char* smem, int st) { return smem + st 
 template <int D>
 __device__ __forceinline__ char* v_stage(char* smem, int st) { return smem + (2 + st) * Cfg<D>::TILE_BYTES; }
 
+// The four K/V stages as separate LDS objects (K stages 0/1, V stages 0/1;
+// the kernel declares them).  With every stage its own object and the stage
+// index a compile-time constant, the compiler can tell that a read of one
+// stage does not alias a buffer-to-LDS copy in flight into another, and does
+// not wait for those copies before the read; with the stages as parts of
+// one array it waits for every copy in flight.
+template <int D>
+struct KVStages {
+  char* k[2];
+  char* v[2];
+  // LDS region of wave wv for store_rows: the stages in the order K0, K1,
+  // V0, V1, each holding TILE_BYTES / (32 CPR 16) waves' regions.
+  __device__ __forceinline__ char* region(int wv) const {
+    constexpr int kRegion = 32 * Cfg<D>::CPR * 16;
+    constexpr int kPer = Cfg<D>::TILE_BYTES / kRegion;
+    static_assert(kPer >= 1 && 4 * kPer >= kWaves, "output staging must fit the K/V stages");
+    const int obj = wv / kPer;
+    char* base = obj == 0 ? k[0] : obj == 1 ? k[1] : obj == 2 ? v[0] : v[1];
+    return base + (wv - obj * kPer) * kRegion;
+  }
+};
+
 // Calls f(std::integral_constant<int, D>{}) for a supported head_dim d
 // (a multiple of 32 from 32 to 256) and returns its status.
 // ATTN_ONLY_D: instantiate that head_dim alone (the second forward
@@ -754,7 +776,7 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kS
 // ([CANN-FA] section "Ascend C implementation": load the next block while the
 // current one is computed).
 template <int D, bool CAUSAL, int PAR, typename T = _Float16, bool UNIFORM = false>
-__device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
+__device__ __forceinline__ void pipeline_step(int j, int nt, const KVStages<D>& st,
                                               __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
                                               const LoadOffsets<D>& lo, int tid, WaveState<D>& w,
                                               STile<D>& s_cur, STile<D>& s_nxt) {
@@ -767,13 +789,13 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
   // instead of ahead of it: +4-5 % for the forward at d = 64 without the
   // mask, -1 to -6 % at the other head_dims, which keep the runtime test.
   if (UNIFORM || j < w.nt_w) {
-    load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), v_base, lo, tid);
-    load_tile<D>(krs, k_stage<D>(smem, PAR), k_base, lo, tid);
+    load_tile<D>(vrs, st.v[PAR ^ 1], v_base, lo, tid);
+    load_tile<D>(krs, st.k[PAR], k_base, lo, tid);
     paranoid_sync();
     // S_{j+1} is computed even past this wave's last tile (reading a stale
     // but in-bounds stage) so that the matrix and vector work stay in one
     // block the scheduler can interleave; it is discarded then.
-    qk_tile<D, T>(k_stage<D>(smem, PAR ^ 1), w.qf, w.off, s_nxt);
+    qk_tile<D, T>(st.k[PAR ^ 1], w.qf, w.off, s_nxt);
     PTile<D> pf;
     softmax_tile<D, T>(s_cur, w.c, w.m_run, pf);
     // Materialise P_j here, so that the compiler keeps the softmax next to
@@ -806,7 +828,7 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
     // P_j V_j, so that the other wave of the SIMD fills the gaps with its
     // vector work rather than the reverse.
     __builtin_amdgcn_s_setprio(1);
-    pv_tile<D, T>(v_stage<D>(smem, PAR), pf, w.off, w.oacc);
+    pv_tile<D, T>(st.v[PAR], pf, w.off, w.oacc);
     add_row_sums<D, T>(pf, w.l_run);
     float m_tile[C::QB];
     tile_max<D>(s_nxt, w.c, m_tile);
@@ -826,8 +848,8 @@ __device__ __forceinline__ void pipeline_step(int j, int nt, char* smem,
     if (j + 1 < w.nt_w) raise_max<D>(m_tile, w.m_run, w.l_run, w.oacc);
     paranoid_sync();
   } else {
-    load_tile<D>(vrs, v_stage<D>(smem, PAR ^ 1), v_base, lo, tid);
-    load_tile<D>(krs, k_stage<D>(smem, PAR), k_base, lo, tid);
+    load_tile<D>(vrs, st.v[PAR ^ 1], v_base, lo, tid);
+    load_tile<D>(krs, st.k[PAR], k_base, lo, tid);
     paranoid_sync();
     paranoid_sync();
   }
