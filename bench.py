@@ -25,6 +25,11 @@ line with the throughput, the roofline of the kernel (timed with HIP events on
 the launch stream), the CPU oracle timed on a bounded sample of the same
 workload, and a parity check of the timed output against that sample.
 
+    python bench.py --cold 50
+
+also times 50 steps each after a 512 MiB write that evicts the inputs from the
+256 MB last-level cache (a secondary "cold" object; the default is warm).
+
     python bench.py --backward [--workload 2]
 
 times the backward pass instead: a step is one attn_bwd call (two kernels)
@@ -167,6 +172,49 @@ class ClockProbe:
         rec.update(mhz=round(cycles / (ticks / (self.khz * 1e3)) / 1e6, 1) if ticks > 0 else None,
                    window_ms=round(ticks / self.khz, 3))
         return rec
+
+
+def device_peak() -> dict:
+    """The dense fp16 matrix peak from the device's own figures: compute units
+    x maximum shader clock x 4 096 FLOP per CU per clock (4 SIMDs, one
+    32x32x16 fp16 MFMA of 32 768 FLOP per 32 clocks each)."""
+    import ctypes
+
+    from exact_attention_121_amd.build import PROBE_PATH
+
+    try:
+        lib = ctypes.CDLL(PROBE_PATH)
+        cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+        if lib.attn_device_info(ctypes.byref(cus), ctypes.byref(khz)) != 0:
+            raise OSError("attn_device_info failed")
+    except (OSError, AttributeError) as e:
+        return {"tflops": None, "error": str(e)}
+    return {"cus": cus.value, "max_mhz": khz.value / 1e3,
+            "tflops": round(cus.value * khz.value * 1e3 * 4096 / 1e12, 1),
+            "source": "hipDeviceAttributeMultiprocessorCount x hipDeviceAttributeClockRate x 4096 FLOP/CU/clk"}
+
+
+def cold_steps(step, dev, steps: int, flush_mib: int = 512) -> dict:
+    """Kernel time of `steps` forward steps, each after writing a flush_mib
+    buffer (larger than the 256 MB last-level cache), so that the step reads
+    its inputs from HBM; HIP events around each step only."""
+    import torch
+
+    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    for i in range(steps):
+        buf.fill_(i & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del buf
+    times.sort()
+    return {"steps": steps, "median_ms": round(times[len(times) // 2], 5), "min_ms": round(times[0], 5),
+            "flush_bytes": flush_mib << 20}
 
 
 def counter_clock(workload_name: str, path=TRAFFIC_FILE, sources=FORWARD_SOURCES):
@@ -649,6 +697,9 @@ def main() -> int:
                          "calibrated against a kernel of known traffic")
     ap.add_argument("--no-gemm-reference", action="store_true",
                     help="skip the fp16 GEMM reference measured after the timed steps")
+    ap.add_argument("--cold", type=int, default=0,
+                    help="forward: also time this many steps each after a 512 MiB write that evicts the inputs "
+                         "from the last-level cache (reported as a secondary 'cold' object)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -716,6 +767,11 @@ def main() -> int:
         "sclk": {"live": live_clock, "counters": counter_clock(w.name) if args.dtype == "f16" else None},
         "kernel_code_sha256_16": kernel_source_hash(),
     }
+    result["roofline"]["peak_from_device"] = device_peak()
+    if args.cold > 0:
+        cold = cold_steps(step, dev, args.cold)
+        cold["tflops_median"] = round(w.flops / (cold["median_ms"] * 1e-3) / 1e12, 2)
+        result["cold"] = cold
     if not args.no_gemm_reference:
         g = gemm_reference(dev)
         g["attention_over_gemm"] = round(value / g["tflops"], 4)

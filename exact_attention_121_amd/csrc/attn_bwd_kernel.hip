@@ -451,7 +451,12 @@ template <int D, bool CAUSAL, typename T>
 __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_kernel(BwdParams p, int q_tiles) {
   using C = Cfg<D>;
   static_assert(C::QB == 1, "one 32-row block per wave");
+  // K stages 0/1 then V stages 0/1 in one array.  (As separate objects,
+  // which drops the compiler's waits for copies in flight before reads of
+  // the other stages, the backward steps measured -3 % at d = 64 and within
+  // 0.5 % elsewhere.)
   __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
+  const KVStages<D> kv{{smem, smem + C::TILE_BYTES}, {smem + 2 * C::TILE_BYTES, smem + 3 * C::TILE_BYTES}};
 
   // As in the forward: causal query tiles heaviest first across a group of
   // heads.
@@ -524,8 +529,8 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
     nt_w = last_w / C::BN + 1;
   }
 
-  load_tile<D>(krs, k_stage<D>(smem, 0), 0, lo, tid);
-  load_tile<D>(vrs, v_stage<D>(smem, 0), 0, lo, tid);
+  load_tile<D>(krs, kv.k[0], 0, lo, tid);
+  load_tile<D>(vrs, kv.v[0], 0, lo, tid);
   wait_vm_all();
   __syncthreads();
   // One key tile per step; the stage is a compile-time constant in the
@@ -533,13 +538,13 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
   auto step = [&](auto stc, int j) {
     const int st = stc;
     const uint32_t nb = tile_base<D>(j + 1, nt);
-    load_tile<D>(krs, k_stage<D>(smem, st ^ 1), nb, lo, tid);
-    load_tile<D>(vrs, v_stage<D>(smem, st ^ 1), nb, lo, tid);
+    load_tile<D>(krs, kv.k[st ^ 1], nb, lo, tid);
+    load_tile<D>(vrs, kv.v[st ^ 1], nb, lo, tid);
     paranoid_sync();
     if (j < nt_w) {
       STile<D> s, dp;
-      qk_tile<D, T>(k_stage<D>(smem, st), qf, off, s);    // S^T = K Q^T
-      qk_tile<D, T>(v_stage<D>(smem, st), df, off, dp);   // dP^T = V dO^T
+      qk_tile<D, T>(kv.k[st], qf, off, s);    // S^T = K Q^T
+      qk_tile<D, T>(kv.v[st], df, off, dp);   // dP^T = V dO^T
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
 #pragma unroll
@@ -553,22 +558,22 @@ __global__ __launch_bounds__(kThreads, bwd_dq_wg_per_cu<D>()) void attn_bwd_dq_k
         for (int r = 0; r < 16; ++r) dl[t][r] = delta;
       PTile<D> pf, dsf;
       p_and_ds<D, T>(s, dp, dl, pf, dsf);
-      pv_tile<D, T>(k_stage<D>(smem, st), dsf, off, dq_acc);   // dQ^T += K^T dS^T
+      pv_tile<D, T>(kv.k[st], dsf, off, dq_acc);   // dQ^T += K^T dS^T
     }
     paranoid_sync();
     wait_vm_all();
     __syncthreads();
     };
-  // Unrolled by two (at d = 128 this spills 12 bytes per lane, 36 with the
-  // causal mask, and is still faster than the rolled loop: +6.5 % on a
-  // whole backward step, +2-3 % causal).
+  // Unrolled by two (at d = 128 the causal kernel then spills 28 bytes per
+  // lane and is still faster than with the rolled loop: +6.5 % on a whole
+  // backward step, +2-3 % causal).
   for (int j = 0; j < nt; j += 2) {
     step(std::integral_constant<int, 0>{}, j);
     if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // As in the forward: rows staged in the freed stages, coalesced stores.
-  store_rows<D, T>(row_region<D>(smem, wv), dq_acc[0], p.scale, p.dq + qoff + (size_t)qw0 * D, N - qw0, lane);
+  store_rows<D, T>(kv.region(wv), dq_acc[0], p.scale, p.dq + qoff + (size_t)qw0 * D, N - qw0, lane);
 }
 
 template <int D, bool CAUSAL, typename T>

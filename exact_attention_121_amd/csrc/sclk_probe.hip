@@ -1,4 +1,5 @@
-// Shader-clock probe for the benchmark (not part of the attention path).
+// Shader-clock probe and device facts for the benchmark (not part of the
+// attention path).
 //
 // One wave reads the shader-clock cycle counter (clock64) and the
 // constant-rate wall counter (wall_clock64, hipDeviceAttributeWallClockRate
@@ -49,3 +50,12 @@ extern "C" int attn_sclk_probe(unsigned long long* out, unsigned long long wall_
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
+// Compute units and the maximum shader clock (kHz) of the current device, as
+// the runtime reports them (hipDeviceAttributeMultiprocessorCount,
+// hipDeviceAttributeClockRate).  Returns 0, or 1 on error.
+extern "C" int attn_device_info(int* cus, int* max_clock_khz) {
+  int dev = 0;
+  if (cus == nullptr || max_clock_khz == nullptr || hipGetDevice(&dev) != hipSuccess) return 1;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 1;
+  return hipDeviceGetAttribute(max_clock_khz, hipDeviceAttributeClockRate, dev) == hipSuccess ? 0 : 1;
+}

@@ -1,8 +1,9 @@
 """The benchmark's JSON line on the GPU (bench.py run as a child process).
 
-One short forward run with a bounded oracle sample, and one short decode run:
-the line has the fields its contract names, a parity check that passed, and a
-live shader clock in the range the part can run at.
+One short forward run with a bounded oracle sample (and a few cold-cache
+steps), and one short decode run: the line has the fields its contract names,
+a parity check that passed, a live shader clock in the range the part can run
+at, and the device-derived peak.
 """
 
 import json
@@ -32,7 +33,7 @@ def _clock_ok(line):
 
 
 def test_forward_line():
-    line = _bench("--steps", "20", "--warmup", "5", "--cpu-budget", "1", "--no-gemm-reference")
+    line = _bench("--steps", "20", "--warmup", "5", "--cpu-budget", "1", "--no-gemm-reference", "--cold", "5")
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
                 "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline", "kernel_ms", "clock_warmup"):
         assert key in line, key
@@ -41,6 +42,9 @@ def test_forward_line():
     assert line["parity"]["ok"], line["parity"]
     assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] >= 1
     _clock_ok(line)
+    peak = line["roofline"]["peak_from_device"]
+    assert peak["cus"] >= 1 and peak["tflops"] > 0, peak
+    assert line["cold"]["steps"] == 5 and line["cold"]["median_ms"] > 0
 
 
 def test_decode_line():
