@@ -4,6 +4,7 @@
     o, lse = attn_fwd(q, k, v, causal=True)     # torch fp16 tensors on the GPU
     dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=True)
     o1, lse1 = attn_decode(q_new, k_cache, v_cache)
+    o = flash_attention(q, k, v, causal=True)   # differentiable (attn_fwd / attn_bwd)
 
 The computation runs in hand-written HIP kernels behind a C ABI
 (include/attn_fwd.h, libattn_fwd.so); this package is the thin binding,
@@ -34,5 +35,6 @@ from .binding import (  # noqa: F401
     attn_version,
     load_library,
 )
+from .autograd import flash_attention, scaled_dot_product_attention  # noqa: F401
 
 __version__ = "0.4.0"

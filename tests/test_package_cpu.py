@@ -1,8 +1,11 @@
 """Package-level checks on the CPU: the product path never reaches the
-oracle, and the offline tile sweep's variant table is well formed."""
+oracle, the offline tile sweep's variant table is well formed, and the
+differentiable entry points refuse what the kernels do not compute."""
 
 import ast
 import os
+
+import pytest
 
 import exact_attention_121_amd as ea
 
@@ -51,3 +54,22 @@ def test_tile_sweep_run_needs_the_oracle_check(capsys):
     finally:
         sys.argv = argv
     assert "oracle check" in capsys.readouterr().err
+
+
+def test_sdpa_refuses_what_the_kernels_do_not_compute():
+    """scaled_dot_product_attention refuses masks and dropout before any GPU
+    call, and flash_attention, like attn_fwd, refuses host tensors."""
+    import torch
+
+    import exact_attention_121_amd as ea
+
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
+    k = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(NotImplementedError):
+        ea.scaled_dot_product_attention(q, q, q, attn_mask=torch.ones(8, 8, dtype=torch.bool))
+    with pytest.raises(NotImplementedError):
+        ea.scaled_dot_product_attention(q, q, q, dropout_p=0.1)
+    with pytest.raises(ValueError):
+        ea.scaled_dot_product_attention(q, k, k, enable_gqa=False)
+    with pytest.raises(ValueError):
+        ea.flash_attention(q, q, q)
